@@ -1,0 +1,285 @@
+"""Benchmark of the ragged-dot hot path on one MI355X.
+
+One step = the MoE up-projection layer (2048 tokens x top-4 = 8192 rows, 64
+experts with Zipf(1.1) sizes, k = 4096, fused wi n = 2048) forward and
+backward, through every kernel of the path:
+
+    fused  = ragged_dot(x, w, gs)                     [8192, 2048] bf16
+    act    = glu_fwd(fused)                           [8192, 1024]
+    dfused = glu_bwd(fused, d_act)                    [8192, 2048]
+    dx     = ragged_dot(dfused, w, gs, trans_rhs)     [8192, 4096]
+    dw     = trans_ragged_dot(x, dfused, gs)          [64, 4096, 2048] bf16
+
+``value`` is the GEMM work on valid rows (3 x 2 * sum(gs) * k * n FLOP) per
+second of step time.  Inputs are synthetic, seeded and resident in HBM
+before timing.  Every kernel is also timed on its own with HIP events on the
+stream it runs on; the slowest one is reported against its roofline.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, published (no sparsity)
+METRIC = "ragged_dot TFLOP/s (valid rows) + % bf16 MFMA peak; decode-shape HBM GB/s"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
+    ap.add_argument("--all", action="store_true", help="also time the backward, window+limit and decode workloads")
+    return ap.parse_args()
+
+
+def timed_ops(ops, steps, warmup):
+    """Run `warmup` untimed steps, then `steps` timed ones with per-op HIP events."""
+    import torch
+
+    for _ in range(warmup):
+        for _, fn in ops:
+            fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
+           for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        for (_, fn), (a, b) in zip(ops, evs[s]):
+            a.record(stream)
+            fn()
+            b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_op = {}
+    for i, (name, _) in enumerate(ops):
+        per_op[name] = sum(evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(steps)) / steps
+    first, last = evs[0][0][0], evs[-1][-1][1]
+    gpu_ms = first.elapsed_time(last)
+    return wall, gpu_ms, per_op
+
+
+def upproj(steps, warmup):
+    import torch
+
+    from expert_ffn_ragged_amd import rd, workloads
+
+    d = workloads.make(2, "cuda", parts=("x", "w"))
+    x, w, gs = d["x"], d["w"], d["gs"]
+    m, k, n = d["m"], d["k"], d["n"]
+    rows = int(d["gs_host"].sum())
+    d_act = workloads.bf16_normal((m, n // 2), 1.0, 2006, "cuda")
+    fused = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    act = torch.empty((m, n // 2), dtype=torch.bfloat16, device="cuda")
+    dfused = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    dx = torch.empty((m, k), dtype=torch.bfloat16, device="cuda")
+    dw = torch.empty((w.shape[0], k, n), dtype=torch.bfloat16, device="cuda")
+    ops = [
+        ("ragged_dot", lambda: rd.ragged_dot(x, w, gs, out=fused)),
+        ("glu_fwd", lambda: rd.glu_fwd(fused, out=act)),
+        ("glu_bwd", lambda: rd.glu_bwd(fused, d_act, out=dfused)),
+        ("ragged_dot_trans_rhs", lambda: rd.ragged_dot(dfused, w, gs, trans_rhs=True, out=dx)),
+        ("trans_ragged_dot", lambda: rd.trans_ragged_dot(x, dfused, gs, out=dw)),
+    ]
+    wall, gpu_ms, per_op = timed_ops(ops, steps, warmup)
+    gemm_flop = 2.0 * rows * k * n
+    b = 2  # bf16 bytes
+    # algorithmic bytes: every operand read once, every result written once
+    nbytes = {
+        "ragged_dot": rows * k * b + w.numel() * b + rows * n * b,
+        "ragged_dot_trans_rhs": rows * n * b + w.numel() * b + rows * k * b,
+        "trans_ragged_dot": rows * k * b + rows * n * b + w.numel() * b,
+        "glu_fwd": rows * n * b + rows * (n // 2) * b,
+        "glu_bwd": rows * n * b + rows * (n // 2) * b + rows * n * b,
+    }
+    flops = {"ragged_dot": gemm_flop, "ragged_dot_trans_rhs": gemm_flop, "trans_ragged_dot": gemm_flop,
+             "glu_fwd": 0.0, "glu_bwd": 0.0}
+    return dict(rows=rows, m=m, k=k, n=n, G=w.shape[0], wall=wall, gpu_ms=gpu_ms, per_op=per_op,
+                bytes=nbytes, flops=flops, step_flop=3 * gemm_flop,
+                tensors=(x, w, dfused, d["gs_host"]))
+
+
+def roofline(name, ms, nbytes, flop):
+    """Report a kernel against the roof its arithmetic intensity puts it under."""
+    ai = flop / nbytes if nbytes else 0.0
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if flop > 0 and ai >= ridge:
+        achieved = flop / (ms * 1e-3) / 1e12
+        return {"kernel": name, "bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "ms": round(ms, 4), "algorithmic_bytes": int(nbytes), "flop": flop}
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "ms": round(ms, 4),
+            "algorithmic_bytes": int(nbytes), "flop": flop}
+
+
+def extra_workloads(steps):
+    """Single-op timings of the other workloads (reported beside the headline)."""
+    import torch
+
+    from expert_ffn_ragged_amd import rd, workloads
+
+    out = {}
+    d = workloads.make(5, "cuda", parts=("x", "w"))
+    o = torch.empty((d["m"], d["n"]), dtype=torch.bfloat16, device="cuda")
+    _, _, per = timed_ops([("decode", lambda: rd.ragged_dot(d["x"], d["w"], d["gs"], out=o))], steps, 3)
+    nz = d["gs_host"] > 0
+    rows = int(d["gs_host"].sum())
+    nb = rows * d["k"] * 2 + int(nz.sum()) * d["k"] * d["n"] * 2 + rows * d["n"] * 2
+    out["decode_m512_k4096_n1536_g128"] = {"ms": round(per["decode"], 4), "GB/s": round(nb / per["decode"] / 1e6, 1),
+                                            "hbm_frac": round(nb / per["decode"] / 1e6 / HBM_PEAK_GBS, 4)}
+    del d, o
+    torch.cuda.empty_cache()
+    return out
+
+
+def extra_all(steps):
+    import torch
+
+    from expert_ffn_ragged_amd import rd, workloads
+
+    out = {}
+    d = workloads.make(3, "cuda")
+    m, k, n = d["m"], d["k"], d["n"]
+    rows = int(d["gs_host"].sum())
+    dx = torch.empty((m, k), dtype=torch.bfloat16, device="cuda")
+    dw = torch.empty((d["G"], k, n), dtype=torch.bfloat16, device="cuda")
+    dw32 = torch.empty((d["G"], k, n), dtype=torch.float32, device="cuda")
+    _, _, per = timed_ops([
+        ("dx", lambda: rd.ragged_dot(d["dy"], d["w"], d["gs"], trans_rhs=True, out=dx)),
+        ("dw_bf16", lambda: rd.trans_ragged_dot(d["x"], d["dy"], d["gs"], out=dw)),
+        ("dw_f32", lambda: rd.trans_ragged_dot(d["x"], d["dy"], d["gs"], out=dw32)),
+    ], steps, 3)
+    fl = 2.0 * rows * k * n
+    for key, ms in per.items():
+        out[f"backward_m32768_{key}"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1),
+                                        "mfma_frac": round(fl / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    del d, dx, dw, dw32
+    torch.cuda.empty_cache()
+    d = workloads.make(4, "cuda", parts=("x", "w", "fused", "d_out"))
+    off = torch.tensor([96], dtype=torch.int32, device="cuda")
+    lim = torch.tensor([d["limit"]], dtype=torch.int32, device="cuda")
+    o = torch.empty((d["m"], d["n"]), dtype=torch.bfloat16, device="cuda")
+    g = torch.empty((d["m"], d["n"]), dtype=torch.bfloat16, device="cuda")
+    gb = torch.empty((d["m"], 2 * d["n"]), dtype=torch.bfloat16, device="cuda")
+    _, _, per = timed_ops([
+        ("window_ragged_dot", lambda: rd.ragged_dot(d["x"], d["w"], d["gs"], off, lim, out=o)),
+        ("glu_fwd", lambda: rd.glu_fwd(d["fused"], lim, out=g)),
+        ("glu_bwd", lambda: rd.glu_bwd(d["fused"], d["d_out"], lim, out=gb)),
+    ], steps, 3)
+    L, h = d["limit"], d["n"]
+    gsz = d["gs_host"].astype("int64")
+    lo, hi = int(gsz[:96].sum()), int(gsz[:128].sum())
+    win_rows = hi - lo
+    fl = 2.0 * win_rows * d["k"] * d["n"]
+    nb = win_rows * d["k"] * 2 + d["w"].numel() * 2 + L * d["n"] * 2
+    ms = per["window_ragged_dot"]
+    out["window_limit_ragged_dot"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1),
+                                      "GB/s": round(nb / ms / 1e6, 1)}
+    for key, nbytes in (("glu_fwd", L * h * 6), ("glu_bwd", L * h * 10)):
+        out[f"window_limit_{key}"] = {"ms": round(per[key], 4), "GB/s": round(nbytes / per[key] / 1e6, 1),
+                                      "hbm_frac": round(nbytes / per[key] / 1e6 / HBM_PEAK_GBS, 4)}
+    return out
+
+
+def cpu_baseline(x, w, dy, gs_host, budget_s=12.0):
+    """The CPU oracle, as it stands, on a bounded sample of the timed workload.
+
+    Runs the oracle's ragged_dot, trans_rhs ragged_dot and trans_ragged_dot
+    expert by expert on the same tensors the GPU just processed (copied to the
+    host one expert at a time) until about ``budget_s`` seconds are spent.
+    """
+    import numpy as np
+
+    import oracle
+    from expert_ffn_ragged_amd.workloads import bits
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity set numpy's BLAS defaults to
+        cores = len(os.sched_getaffinity(0))
+    lb = np.concatenate([[0], np.cumsum(gs_host)])
+    k, n = w.shape[1], w.shape[2]
+    spent, rows, experts = 0.0, 0, 0
+    for j in range(len(gs_host)):
+        r0, r1 = int(lb[j]), int(lb[j + 1])
+        if r1 == r0:
+            continue
+        xb, dyb, wb = bits(x[r0:r1]), bits(dy[r0:r1]), bits(w[j:j + 1])
+        one = np.array([r1 - r0], dtype=np.int32)
+        t0 = time.perf_counter()
+        oracle.ragged_dot(xb, wb, one)
+        oracle.ragged_dot(dyb, wb, one, trans_rhs=True)
+        oracle.trans_ragged_dot(xb, dyb, one)
+        spent += time.perf_counter() - t0
+        rows += r1 - r0
+        experts += 1
+        if spent >= budget_s:
+            break
+    flop = 3 * 2.0 * rows * k * n
+    return {"value": round(flop / spent / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"oracle ragged_dot + trans_rhs ragged_dot + trans_ragged_dot (float64) on the timed "
+                      f"up-projection tensors, {experts} of 64 experts ({rows} of 8192 rows), {spent:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the ragged-dot path runs on a single MI355X here; "
+              "multi-GPU (expert-parallel) runs are not part of this build", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    from expert_ffn_ragged_amd import rd
+
+    rd.library()
+    r = upproj(args.steps, args.warmup)
+    ms_step = r["gpu_ms"] / args.steps
+    value = r["step_flop"] / (ms_step * 1e-3) / 1e12
+    dom = max(r["per_op"], key=r["per_op"].get)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "moe up-projection fwd+bwd: m8192 (2048 tok x top4) k4096 n2048 g64 zipf1.1",
+                   "m": r["m"], "k": r["k"], "n": r["n"], "groups": r["G"], "valid_rows": r["rows"],
+                   "parallelism": "none (1 GPU)"},
+        "pct_bf16_mfma_peak": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
+        "roofline": roofline(dom, r["per_op"][dom], r["bytes"][dom], r["flops"][dom]),
+        "per_kernel": {name: roofline(name, ms, r["bytes"][name], r["flops"][name])
+                       for name, ms in r["per_op"].items()},
+    }
+    line["extra"] = extra_workloads(max(args.steps, 10))
+    if args.all:
+        line["extra"].update(extra_all(max(args.steps, 10)))
+    line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(*r["tensors"])
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

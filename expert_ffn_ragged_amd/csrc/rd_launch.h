@@ -1,0 +1,34 @@
+// Internal launch interface between the C-ABI layer (rd_api.cpp) and the
+// kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace rd {
+
+// One grouped-GEMM call as the host sees it.  Device-resident values
+// (group sizes, offset, limit) stay behind their pointers.
+struct GemmProblem {
+  const void* a;             // forward: x [m,k]; trans: x [m,k]
+  const void* b;             // forward: w [gl,k,n] or [gl,n,k]; trans: dy [m,n]
+  const int32_t* group_sizes;
+  int32_t num_groups;
+  const int32_t* group_offset;  // may be null
+  int32_t num_local;
+  const int32_t* limit;          // may be null
+  void* out;                 // forward: [m,n]; trans: [gl,k,n]
+  bool out_f32;
+  int m, k, n;
+};
+
+int launch_forward(const GemmProblem& p, bool trans_rhs, hipStream_t stream);
+int launch_trans(const GemmProblem& p, hipStream_t stream);
+int launch_glu_fwd(const void* fused, const int32_t* limit, void* out, int rows, int h, hipStream_t stream);
+int launch_glu_bwd(const void* fused, const void* d_out, const int32_t* limit, void* d_fused, int rows, int h,
+                   hipStream_t stream);
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+}  // namespace rd

@@ -1,0 +1,206 @@
+"""Thin ctypes binding over librd.so (include/rd.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  PyTorch supplies device memory and the current
+stream.  There is no fallback: if the library is missing or a call fails,
+an exception is raised.
+
+Device scalars (``group_offset``, ``limit``) are passed as int32 tensors of
+shape ``(1,)`` on the GPU, and ``group_sizes`` as an int32 GPU tensor, so a
+call never reads device data on the host and can be captured in a HIP graph.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librd.so")
+
+RD_OK, RD_EINVAL, RD_EUNSUPPORTED, RD_EHIP = 0, 1, 2, 3
+RD_BF16, RD_F32 = 0, 1
+_DTYPES = {torch.bfloat16: RD_BF16, torch.float32: RD_F32}
+
+EXPORTS = (
+    "rd_abi_version",
+    "rd_status_string",
+    "rd_forward",
+    "rd_forward_trans_rhs",
+    "rd_trans_workspace_size",
+    "rd_trans",
+    "rd_glu_fwd",
+    "rd_glu_bwd",
+)
+
+
+class RDError(RuntimeError):
+    """A nonzero status from librd.so."""
+
+
+_lib = None
+
+
+def library():
+    """The loaded librd.so (loaded once, after torch's HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RDError(f"{LIB_PATH} is not built; run `python -m expert_ffn_ragged_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.rd_abi_version.restype = ctypes.c_int
+    lib.rd_abi_version.argtypes = []
+    lib.rd_status_string.restype = ctypes.c_char_p
+    lib.rd_status_string.argtypes = [ctypes.c_int]
+    fwd = [vp, vp, vp, i32, vp, i32, vp, vp, i32, i64, i64, i64, vp]
+    for name in ("rd_forward", "rd_forward_trans_rhs"):
+        getattr(lib, name).restype = ctypes.c_int
+        getattr(lib, name).argtypes = fwd
+    lib.rd_trans_workspace_size.restype = sz
+    lib.rd_trans_workspace_size.argtypes = [i64, i64, i64, i32]
+    lib.rd_trans.restype = ctypes.c_int
+    lib.rd_trans.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, i32, i64, i64, i64, vp, sz, vp]
+    lib.rd_glu_fwd.restype = ctypes.c_int
+    lib.rd_glu_fwd.argtypes = [vp, vp, vp, i64, i64, vp]
+    lib.rd_glu_bwd.restype = ctypes.c_int
+    lib.rd_glu_bwd.argtypes = [vp, vp, vp, vp, i64, i64, vp]
+    if lib.rd_abi_version() != 1:
+        raise RDError("librd.so ABI version mismatch")
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != RD_OK:
+        raise RDError(library().rd_status_string(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _scalar(t, name):
+    if t is None:
+        return None
+    _need(t, name, torch.int32)
+    if t.numel() != 1:
+        raise ValueError(f"{name} must hold exactly one int32")
+    return t
+
+
+def ragged_dot(x, w, group_sizes, group_offset=None, limit=None, trans_rhs=False,
+               out_dtype=torch.bfloat16, out=None, stream=None):
+    """out[rows of local group j] = x[rows] @ w[j] (or @ w[j].T with trans_rhs).
+
+    x: [m, k] bf16; w: [num_local, k, n] bf16 ([num_local, n, k] with trans_rhs);
+    group_sizes: [G] int32 on the GPU; group_offset, limit: optional (1,) int32
+    GPU tensors.  Rows below the limit outside the local window are +0; rows
+    at or past the limit are left as they were in ``out`` (uninitialised when
+    ``out`` is not given).
+    """
+    _need(x, "x", torch.bfloat16, 2)
+    _need(w, "w", torch.bfloat16, 3)
+    _need(group_sizes, "group_sizes", torch.int32, 1)
+    group_offset = _scalar(group_offset, "group_offset")
+    limit = _scalar(limit, "limit")
+    m, k = x.shape
+    gl = w.shape[0]
+    if trans_rhs:
+        n, kw = w.shape[1], w.shape[2]
+    else:
+        kw, n = w.shape[1], w.shape[2]
+    if kw != k:
+        raise ValueError("contraction sizes of x and w differ")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    _need(out, "out", out.dtype, 2)
+    if tuple(out.shape) != (m, n) or out.dtype not in _DTYPES:
+        raise ValueError("out must be [m, n] bf16 or float32")
+    fn = library().rd_forward_trans_rhs if trans_rhs else library().rd_forward
+    _check(fn(_ptr(x), _ptr(w), _ptr(group_sizes), group_sizes.numel(), _ptr(group_offset), gl,
+              _ptr(limit), _ptr(out), _DTYPES[out.dtype], m, k, n, _stream(stream)))
+    return out
+
+
+def trans_ragged_dot(x, dy, group_sizes, num_local=None, group_offset=None, limit=None,
+                     out_dtype=torch.float32, out=None, workspace=None, stream=None):
+    """dw[j] = x_j^T @ dy_j over the rows of local group j; [num_local, k, n]."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(dy, "dy", torch.bfloat16, 2)
+    _need(group_sizes, "group_sizes", torch.int32, 1)
+    group_offset = _scalar(group_offset, "group_offset")
+    limit = _scalar(limit, "limit")
+    m, k = x.shape
+    if dy.shape[0] != m:
+        raise ValueError("x and dy must have the same rows")
+    n = dy.shape[1]
+    gl = group_sizes.numel() if num_local is None else int(num_local)
+    if out is None:
+        out = torch.empty((gl, k, n), dtype=out_dtype, device=x.device)
+    _need(out, "out", out.dtype, 3)
+    if tuple(out.shape) != (gl, k, n) or out.dtype not in _DTYPES:
+        raise ValueError("out must be [num_local, k, n] bf16 or float32")
+    lib = library()
+    ws_bytes = lib.rd_trans_workspace_size(m, k, n, gl)
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    _check(lib.rd_trans(_ptr(x), _ptr(dy), _ptr(group_sizes), group_sizes.numel(), _ptr(group_offset), gl,
+                        _ptr(limit), _ptr(out), _DTYPES[out.dtype], m, k, n,
+                        _ptr(workspace) if ws_bytes else None, ws_bytes, _stream(stream)))
+    return out
+
+
+def glu_fwd(fused, limit=None, out=None, stream=None):
+    """out[r, c] = bf16(silu(gate) * up) for rows r < limit; fused is [rows, 2h] as [gate | up]."""
+    _need(fused, "fused", torch.bfloat16, 2)
+    limit = _scalar(limit, "limit")
+    rows, two_h = fused.shape
+    if two_h % 2:
+        raise ValueError("fused width must be even")
+    h = two_h // 2
+    if out is None:
+        out = torch.empty((rows, h), dtype=torch.bfloat16, device=fused.device)
+    _need(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (rows, h):
+        raise ValueError("out must be [rows, h]")
+    _check(library().rd_glu_fwd(_ptr(fused), _ptr(limit), _ptr(out), rows, h, _stream(stream)))
+    return out
+
+
+def glu_bwd(fused, d_out, limit=None, out=None, stream=None):
+    """[d_gate | d_up] for rows r < limit, -0 written as +0; returns [rows, 2h] bf16."""
+    _need(fused, "fused", torch.bfloat16, 2)
+    _need(d_out, "d_out", torch.bfloat16, 2)
+    limit = _scalar(limit, "limit")
+    rows, two_h = fused.shape
+    h = two_h // 2
+    if tuple(d_out.shape) != (rows, h):
+        raise ValueError("d_out must be [rows, h]")
+    if out is None:
+        out = torch.empty((rows, two_h), dtype=torch.bfloat16, device=fused.device)
+    _need(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (rows, two_h):
+        raise ValueError("out must be [rows, 2h]")
+    _check(library().rd_glu_bwd(_ptr(fused), _ptr(d_out), _ptr(limit), _ptr(out), rows, h, _stream(stream)))
+    return out

@@ -1,0 +1,169 @@
+/*
+ * rd.h -- C ABI of librd.so: ragged dot (grouped GEMM) for mixture-of-experts
+ * expert FFNs, and the limit-aware silu(gate) * up GLU, on MI355X (gfx950).
+ *
+ * Sources of the operations (the pages these entry points implement):
+ *   [SkyRL]   SkyRL-tx PR #867, "Integrate ragged_dot pallas kernel with
+ *             group_offset support": ragged_dot, its trans_rhs form,
+ *             trans_ragged_dot, the VJP rules in the review, and the
+ *             group_offset window of the suggested fast_ragged_dot.
+ *   [MaxText] MaxText PR #5760, "397B v7x trainer: MoE wo FSDP sharding and
+ *             valid-rows-only MoE kernels", commit on valid rows: the
+ *             packed-buffer row limit and the glu_rows forward/backward.
+ *   [TE]      TransformerEngine PR #2213, "Async issuing D2H memcpy for
+ *             grouped_gemm group_sizes array", Description: copying
+ *             group_sizes to the host stalls the GPU and breaks graph capture.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are device pointers to contiguous row-major arrays, 16-byte
+ *   aligned, owned by the caller.  The library allocates nothing per call,
+ *   keeps no per-call state, and is reentrant.
+ * - bf16 means IEEE binary32 truncated to its high 16 bits (bfloat16).
+ * - group_sizes, group_offset and limit are DEVICE scalars/arrays (int32).
+ *   The host never reads them: no device-to-host copy and no synchronisation
+ *   happens inside any call ([TE]), so every call may be captured in a HIP
+ *   graph and replayed after group_sizes changes on the device.
+ * - Every call enqueues its kernels on `stream` (a hipStream_t; NULL is the
+ *   legacy default stream) and returns without waiting.
+ * - Return value: RD_OK, or a nonzero status.  Problems visible on the host
+ *   (null pointers, bad sizes, misalignment, unknown dtype) are reported
+ *   before anything is launched; a launch failure reports RD_EHIP.  Faults
+ *   of enqueued work surface at the caller's next synchronisation, as usual
+ *   for HIP.  Device-side values never cause out-of-bounds accesses; they
+ *   are clamped as follows:
+ *     * a negative group size counts as 0;
+ *     * L = clamp(*limit, 0, m) (m when limit is NULL);
+ *     * group boundaries are the exclusive prefix sums of the sizes,
+ *       clamped to [0, L]; rows beyond the sum of the sizes belong to no
+ *       group;
+ *     * a window that does not fit (offset < 0 or offset + num_local >
+ *       num_groups) is empty.
+ */
+#ifndef RD_H
+#define RD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RD_ABI_VERSION 1
+
+/* status codes */
+#define RD_OK 0
+#define RD_EINVAL 1        /* a host-visible argument is invalid           */
+#define RD_EUNSUPPORTED 2  /* valid but outside what the kernels support   */
+#define RD_EHIP 3          /* the HIP runtime reported an error            */
+
+/* element types */
+#define RD_BF16 0
+#define RD_F32 1
+
+/* largest num_groups (and num_local) the device-side schedule handles */
+#define RD_MAX_GROUPS 1024
+
+/* Version of this ABI (RD_ABI_VERSION). */
+int rd_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char* rd_status_string(int status);
+
+/*
+ * ragged_dot ([SkyRL]; window from fast_ragged_dot; limit from [MaxText]).
+ *
+ *   x            [m, k] bf16: rows sorted by group.
+ *   w            [num_local, k, n] bf16: one matrix per LOCAL group.
+ *   group_sizes  [num_groups] int32 on the device.
+ *   group_offset NULL, or [1] int32 on the device: index of the first local
+ *                group.  NULL means offset 0 and requires
+ *                num_local == num_groups.
+ *   limit        NULL, or [1] int32 on the device: only rows [0, L) of x
+ *                and out are valid (a packed expert buffer).
+ *   out          [m, n], out_dtype RD_BF16 or RD_F32.
+ *
+ * With b[] the clamped boundaries and off the offset, rows r in
+ * [b[off+j], b[off+j+1]) get out[r,:] = x[r,:] @ w[j] (fp32 accumulation,
+ * then one rounding to out_dtype, round-to-nearest-even for bf16).  Every
+ * other row below L is written as +0.  Rows >= L are neither read (in x)
+ * nor written (in out).
+ *
+ * Requirements: m >= 0; k, n > 0 and multiples of 8; 1 <= num_local <=
+ * num_groups <= RD_MAX_GROUPS; m, k, n < 2^31.  With m == 0 nothing is
+ * launched and x, out may be NULL.
+ */
+int rd_forward(const void* x, const void* w, const int32_t* group_sizes, int32_t num_groups,
+               const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* out,
+               int32_t out_dtype, int64_t m, int64_t k, int64_t n, void* stream);
+
+/*
+ * ragged_dot with trans_rhs ([SkyRL], the dx rule of the backward):
+ * identical to rd_forward except that w is [num_local, n, k] and
+ * out[r,:] = x[r,:] @ w[j]^T, i.e. the contraction runs over w's last dim.
+ */
+int rd_forward_trans_rhs(const void* x, const void* w, const int32_t* group_sizes,
+                         int32_t num_groups, const int32_t* group_offset, int32_t num_local,
+                         const int32_t* limit, void* out, int32_t out_dtype, int64_t m, int64_t k,
+                         int64_t n, void* stream);
+
+/*
+ * trans_ragged_dot ([SkyRL], _gpu_trans_ragged_dot_fwd; the weight
+ * gradient): dw[j] = x_j^T @ dy_j over the rows of local group j.
+ *
+ *   x   [m, k] bf16,  dy [m, n] bf16,  dw [num_local, k, n] (RD_BF16 or RD_F32).
+ *   group_sizes, group_offset, limit: as for rd_forward.
+ *
+ * Rows outside a group's [b[off+j], b[off+j+1]) contribute nothing: they are
+ * removed by selection, so NaN or garbage there (e.g. rows >= L of a packed
+ * buffer, [MaxText]) cannot reach dw.  A local group with no rows gets an
+ * all +0 dw[j].  Rows >= L are never read.
+ *
+ * With m == 0, x and dy may be NULL and every dw[j] is written as +0.
+ *
+ * workspace/workspace_bytes: caller-owned device scratch of at least
+ * rd_trans_workspace_size(...) bytes (may be NULL when that size is 0).
+ */
+size_t rd_trans_workspace_size(int64_t m, int64_t k, int64_t n, int32_t num_local);
+int rd_trans(const void* x, const void* dy, const int32_t* group_sizes, int32_t num_groups,
+             const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* dw,
+             int32_t dw_dtype, int64_t m, int64_t k, int64_t n, void* workspace,
+             size_t workspace_bytes, void* stream);
+
+/*
+ * GLU forward over the valid rows ([MaxText], glu_rows forward).
+ *
+ *   fused [rows, 2h] bf16 laid out as [gate | up] along the columns.
+ *   out   [rows, h] bf16.
+ *   limit NULL (all rows) or [1] int32 on the device.
+ *
+ * For r < L: out[r,c] = bf16(g / (1 + exp(-g)) * u), g = fused[r,c],
+ * u = fused[r,h+c], evaluated in float32 in exactly that order (negate, exp,
+ * +1, divide, multiply) with a correctly rounded divide, the device exp, no
+ * denormal flushing and no contraction into FMA; only the result is rounded
+ * (RNE).  Rows >= L are neither read nor written.  h > 0, multiple of 8.
+ */
+int rd_glu_fwd(const void* fused, const int32_t* limit, void* out, int64_t rows, int64_t h,
+               void* stream);
+
+/*
+ * GLU backward over the valid rows ([MaxText], glu_rows backward).
+ *
+ *   fused   [rows, 2h] bf16 [gate | up];  d_out [rows, h] bf16.
+ *   d_fused [rows, 2h] bf16 written as [d_gate | d_up] in one pass.
+ *
+ * For r < L, in float32 with s = 1 / (1 + exp(-g)):
+ *   d_up   = d * (g / (1 + exp(-g)))
+ *   d_gate = ((d * u) * s) * (1 + g * (1 - s))
+ * each rounded once (RNE), then -0 is written as +0 in both halves.
+ * Rows >= L are neither read nor written.  h > 0, multiple of 8.
+ */
+int rd_glu_bwd(const void* fused, const void* d_out, const int32_t* limit, void* d_fused,
+               int64_t rows, int64_t h, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RD_H */

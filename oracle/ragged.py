@@ -103,10 +103,11 @@ def ragged_dot(x, w, group_sizes, group_offset=None, limit=None, trans_rhs=False
     if rows.size and (rows.min() < 0 or rows.max() >= L):
         raise ValueError("requested rows must lie in [0, L)")
     out = np.zeros((rows.size, n), dtype=np.float64)
-    for i, r in enumerate(rows):
-        if lo <= r < hi:
-            j = int(np.searchsorted(lb, r, side="right")) - 1
-            out[i] = bf16_bits_to_f64(x[r]) @ weight(j)
+    inside = (rows >= lo) & (rows < hi)
+    owner = np.searchsorted(lb, rows, side="right") - 1
+    for j in np.unique(owner[inside]):
+        sel = np.nonzero(inside & (owner == j))[0]
+        out[sel] = bf16_bits_to_f64(x[rows[sel]]) @ weight(int(j))
     return out
 
 

@@ -1,0 +1,97 @@
+"""The C-ABI library: it loads, exports every function include/rd.h declares,
+shares torch's HIP runtime, and rejects host-visible bad arguments before
+launching anything.  Runs without a GPU (no compute call is made)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from expert_ffn_ragged_amd import rd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rd.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rd_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rd.LIB_PATH):
+        pytest.fail("librd.so is not built (run __graft_entry__.build())")
+    return rd.library()
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(rd.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", rd.LIB_PATH], stdout=subprocess.PIPE, text=True).stdout
+    exported = set(re.findall(r"\bT (rd_[a-z_0-9]+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_links_the_same_hip_runtime_soname_as_torch():
+    needed = subprocess.run(["readelf", "-d", rd.LIB_PATH], stdout=subprocess.PIPE, text=True).stdout
+    assert "libamdhip64.so.7" in needed
+
+
+def test_version_and_status_strings(lib):
+    assert lib.rd_abi_version() == 1
+    for s in (0, 1, 2, 3, 99):
+        assert isinstance(lib.rd_status_string(s), bytes)
+    assert lib.rd_trans_workspace_size(100, 64, 64, 4) == 0
+
+
+def _fwd(lib, **kw):
+    a = dict(x=16, w=16, gs=16, G=4, off=None, gl=4, limit=None, out=16, dt=0, m=8, k=8, n=8)
+    a.update(kw)
+    v = lambda p: None if p is None else ctypes.c_void_p(p)
+    return lib.rd_forward(v(a["x"]), v(a["w"]), v(a["gs"]), a["G"], v(a["off"]), a["gl"], v(a["limit"]),
+                          v(a["out"]), a["dt"], a["m"], a["k"], a["n"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), rd.RD_EINVAL),
+    (dict(out=None), rd.RD_EINVAL),
+    (dict(gs=None), rd.RD_EINVAL),
+    (dict(x=24), rd.RD_EINVAL),            # misaligned
+    (dict(gs=18), rd.RD_EINVAL),           # misaligned int32
+    (dict(k=12), rd.RD_EUNSUPPORTED),      # k not a multiple of 8
+    (dict(n=0), rd.RD_EINVAL),
+    (dict(m=-1), rd.RD_EINVAL),
+    (dict(dt=7), rd.RD_EINVAL),
+    (dict(gl=3), rd.RD_EINVAL),            # no offset needs num_local == num_groups
+    (dict(gl=5, off=16), rd.RD_EINVAL),    # num_local > num_groups
+    (dict(G=2000, gl=2000), rd.RD_EUNSUPPORTED),
+    (dict(G=0, gl=0), rd.RD_EINVAL),
+    (dict(m=1 << 31), rd.RD_EUNSUPPORTED),
+    (dict(m=0), rd.RD_OK),                 # nothing to do, nothing launched
+])
+def test_forward_rejects_bad_arguments_before_launch(lib, kw, status):
+    assert _fwd(lib, **kw) == status
+
+
+def test_glu_rejects_bad_arguments(lib):
+    v = ctypes.c_void_p
+    assert lib.rd_glu_fwd(v(16), None, v(16), 4, 12, None) == rd.RD_EUNSUPPORTED
+    assert lib.rd_glu_fwd(None, None, v(16), 4, 8, None) == rd.RD_EINVAL
+    assert lib.rd_glu_fwd(v(16), None, v(16), 0, 8, None) == rd.RD_OK
+    assert lib.rd_glu_bwd(v(16), v(16), None, v(20), 4, 8, None) == rd.RD_EINVAL
+    assert lib.rd_glu_bwd(v(16), v(16), v(18), v(16), 4, 8, None) == rd.RD_EINVAL
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(rd, "_lib", None)
+    monkeypatch.setattr(rd, "LIB_PATH", "/nonexistent/librd.so")
+    with pytest.raises(rd.RDError):
+        rd.library()

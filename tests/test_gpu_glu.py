@@ -1,0 +1,109 @@
+"""GPU parity of the limit-aware GLU forward and backward against the oracle (1 bf16 ulp)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from expert_ffn_ragged_amd import rd, workloads
+from expert_ffn_ragged_amd.workloads import bf16_normal, bits
+from oracle.bf16 import f32_to_bf16_bits
+from tests.gpu_util import assert_glu_close, is_sentinel, say, sentinel
+from tests.test_oracle_glu import FWD_TABLE
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def to_dev(bits16):
+    return torch.from_numpy(np.ascontiguousarray(bits16).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def dev_i32(v):
+    return torch.tensor([int(v)], dtype=torch.int32, device=DEV)
+
+
+def test_every_gate_pattern():
+    """All 65536 bf16 gates (row r holds gate pattern r) against 64 random up / d values."""
+    say("glu all-gate sweep")
+    rng = np.random.default_rng(1)
+    h = 64
+    gates = np.repeat(np.arange(65536, dtype=np.uint32).astype(np.uint16)[:, None], h, axis=1)
+    ups = np.broadcast_to(f32_to_bf16_bits(rng.standard_normal(h).astype(np.float32)), (65536, h))
+    fused = np.concatenate([gates, ups], axis=1)
+    d_out = np.broadcast_to(f32_to_bf16_bits(rng.standard_normal(h).astype(np.float32)), (65536, h))
+    f, d = to_dev(fused), to_dev(d_out)
+    out = rd.glu_fwd(f)
+    dg = rd.glu_bwd(f, d)
+    torch.cuda.synchronize()
+    got_f = bits(out)
+    got_b = bits(dg)
+    assert_glu_close(got_f, oracle.glu_fwd(fused), "glu fwd sweep")
+    assert_glu_close(got_b, oracle.glu_bwd(fused, d_out), "glu bwd sweep")
+    assert not np.any(got_b == 0x8000)
+    # forward keeps IEEE signs: the same rows give -0 where the oracle gives -0
+    want = oracle.glu_fwd(fused)
+    assert np.array_equal(got_f[want == 0x8000], want[want == 0x8000])
+
+
+@pytest.mark.parametrize("g,u,want,why", FWD_TABLE)
+def test_special_values(g, u, want, why):
+    say(f"glu special g={g:#06x} u={u:#06x}")
+    fused = np.zeros((1, 16), dtype=np.uint16)
+    fused[0, :8] = g
+    fused[0, 8:] = u
+    out = bits(rd.glu_fwd(to_dev(fused)))
+    assert_glu_close(out, oracle.glu_fwd(fused), why)
+    if want != "nan":
+        assert np.all(out == want), why
+
+
+@pytest.mark.parametrize("limit", [None, 0, 1, 999, 1000, 5000, -3])
+def test_limit_and_untouched_tail(limit):
+    say(f"glu limit={limit}")
+    rows, h = 1000, 136
+    fused = bf16_normal((rows, 2 * h), 2.0, 7, DEV, nan_rows_from=600 if limit in (1, 999) else None)
+    d_out = bf16_normal((rows, h), 1.0, 8, DEV)
+    lim = None if limit is None else dev_i32(limit)
+    L = rows if limit is None else min(max(limit, 0), rows)
+    out = sentinel((rows, h), torch.bfloat16)
+    dfu = sentinel((rows, 2 * h), torch.bfloat16)
+    rd.glu_fwd(fused, lim, out=out)
+    rd.glu_bwd(fused, d_out, lim, out=dfu)
+    torch.cuda.synchronize()
+    assert_glu_close(bits(out[:L]), oracle.glu_fwd(bits(fused), limit), "fwd")
+    assert_glu_close(bits(dfu[:L]), oracle.glu_bwd(bits(fused), bits(d_out), limit), "bwd")
+    assert bool(is_sentinel(out[L:]).all()) and bool(is_sentinel(dfu[L:]).all())
+
+
+def test_full_packed_buffer():
+    """[225280, 2048] fused buffer, limit 126156, NaN rows past it: sampled rows + untouched tail."""
+    say("full workload: glu fwd/bwd on [225280,2048] limit 126156")
+    d = workloads.make(4, DEV, parts=("fused", "d_out"))
+    L = d["limit"]
+    lim = dev_i32(L)
+    rows, two_h = d["fused"].shape
+    out = sentinel((rows, two_h // 2), torch.bfloat16)
+    dfu = sentinel((rows, two_h), torch.bfloat16)
+    rd.glu_fwd(d["fused"], lim, out=out)
+    rd.glu_bwd(d["fused"], d["d_out"], lim, out=dfu)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4)
+    sel = np.unique(np.concatenate([rng.integers(0, L, 2000), [0, L - 1]]))
+    idx = torch.from_numpy(sel).to(DEV)
+    fs, ds = bits(d["fused"][idx]), bits(d["d_out"][idx])
+    assert_glu_close(bits(out[idx]), oracle.glu_fwd(fs), "full fwd")
+    assert_glu_close(bits(dfu[idx]), oracle.glu_bwd(fs, ds), "full bwd")
+    assert not bool((dfu[:L].view(torch.int16) == -32768).any())
+    assert bool(is_sentinel(out[L:]).all()) and bool(is_sentinel(dfu[L:]).all())
+
+
+def test_full_up_projection_glu():
+    """GLU over the [8192, 2048] output of the MoE up-projection, every element."""
+    say("full workload: glu on [8192,2048]")
+    d = workloads.make(2, DEV, parts=("x", "w"))
+    fused = rd.ragged_dot(d["x"], d["w"], d["gs"])
+    out = rd.glu_fwd(fused)
+    torch.cuda.synchronize()
+    assert_glu_close(bits(out), oracle.glu_fwd(bits(fused)), "up-proj glu")

@@ -1,0 +1,304 @@
+"""GPU parity of ragged_dot, its trans_rhs form and trans_ragged_dot against the oracle.
+
+Small cases compare every element; the full-size workloads compare sampled
+rows the oracle computes one by one, plus properties checked over the whole
+output (zero rows outside the window, untouched rows past the limit, bf16
+output equal to RNE of the float32 output).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from expert_ffn_ragged_amd import rd, workloads
+from expert_ffn_ragged_amd.workloads import bits, bf16_normal
+from tests.gpu_util import (assert_bf16_is_rne_of_f32, assert_gemm_close, is_pos_zero, is_sentinel, say,
+                            sentinel)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def dev_i32(v):
+    return torch.tensor([int(v)], dtype=torch.int32, device=DEV)
+
+
+def run_forward(x, w, gs, off=None, limit=None, trans_rhs=False):
+    """Both output dtypes on sentinel-filled buffers."""
+    m = x.shape[0]
+    n = w.shape[1] if trans_rhs else w.shape[2]
+    o32 = sentinel((m, n), torch.float32)
+    o16 = sentinel((m, n), torch.bfloat16)
+    offt = None if off is None else dev_i32(off)
+    limt = None if limit is None else dev_i32(limit)
+    rd.ragged_dot(x, w, gs, offt, limt, trans_rhs=trans_rhs, out=o32)
+    rd.ragged_dot(x, w, gs, offt, limt, trans_rhs=trans_rhs, out=o16)
+    torch.cuda.synchronize()
+    return o32, o16
+
+
+def check_forward_full(x, w, gs_host, off, limit, trans_rhs, o32, o16, what):
+    """Every element of a small case against the oracle, plus the row contract."""
+    m = x.shape[0]
+    lb, lo, hi, L = oracle.boundaries(gs_host, m, off, w.shape[0], limit)
+    ref = oracle.ragged_dot(bits(x), bits(w), gs_host, off, limit, trans_rhs)
+    got = o32.cpu().numpy()
+    assert_gemm_close(got[:L], ref, what)
+    # rows outside the window below L are exact +0; rows >= L untouched
+    outside = np.ones(L, dtype=bool)
+    outside[lo:hi] = False
+    assert bool(is_pos_zero(o32[:L][torch.from_numpy(outside).to(DEV)]).all()), what + ": non-+0 masked rows"
+    assert bool(is_pos_zero(o16[:L][torch.from_numpy(outside).to(DEV)]).all()), what + ": non-+0 masked rows"
+    assert bool(is_sentinel(o32[L:]).all()) and bool(is_sentinel(o16[L:]).all()), what + ": rows >= L written"
+    assert_bf16_is_rne_of_f32(o16[:L], o32[:L], what)
+
+
+# ------------------------------------------------------------ tiny workload (all positions of the empty group)
+
+@pytest.mark.parametrize("empty_at", [0, 1, 2, 3])
+@pytest.mark.parametrize("trans_rhs", [False, True])
+def test_tiny_ragged_dot(empty_at, trans_rhs):
+    say(f"tiny ragged_dot empty_at={empty_at} trans_rhs={trans_rhs}")
+    gs_host = workloads.group_sizes(1, empty_at=empty_at)
+    assert gs_host.sum() == 256 and gs_host[empty_at] == 0
+    d = workloads.make(1, "cpu")
+    x = d["x"].to(DEV)
+    w = (bf16_normal((4, 256, 128), 128 ** -0.5, 77, "cpu") if trans_rhs else d["w"]).to(DEV)
+    gs = torch.from_numpy(gs_host).to(DEV)
+    o32, o16 = run_forward(x, w, gs, trans_rhs=trans_rhs)
+    check_forward_full(x, w, gs_host, None, None, trans_rhs, o32, o16, "tiny")
+
+
+@pytest.mark.parametrize("empty_at", [0, 1, 2, 3])
+def test_tiny_trans_ragged_dot(empty_at):
+    say(f"tiny trans_ragged_dot empty_at={empty_at}")
+    gs_host = workloads.group_sizes(1, empty_at=empty_at)
+    d = workloads.make(1, "cpu")
+    x, dy = d["x"].to(DEV), d["dy"].to(DEV)
+    gs = torch.from_numpy(gs_host).to(DEV)
+    d32 = sentinel((4, 128, 256), torch.float32)
+    d16 = sentinel((4, 128, 256), torch.bfloat16)
+    rd.trans_ragged_dot(x, dy, gs, out=d32)
+    rd.trans_ragged_dot(x, dy, gs, out=d16)
+    torch.cuda.synchronize()
+    ref = oracle.trans_ragged_dot(bits(x), bits(dy), gs_host)
+    assert_gemm_close(d32.cpu().numpy(), ref, "tiny dW")
+    assert bool(is_pos_zero(d32[empty_at]).all()) and bool(is_pos_zero(d16[empty_at]).all())
+    assert_bf16_is_rne_of_f32(d16, d32, "tiny dW")
+
+
+# ------------------------------------------------------------ windows, limits, ragged tails, degenerate cases
+
+def _case(m, k, n, gs, gl, seed, trans_rhs=False, nan_from=None):
+    x = bf16_normal((m, k), 1.0, seed, "cpu", nan_rows_from=nan_from).to(DEV)
+    shape = (gl, n, k) if trans_rhs else (gl, k, n)
+    w = bf16_normal(shape, 0.05, seed + 1, "cpu").to(DEV)
+    return x, w, torch.tensor(gs, dtype=torch.int32, device=DEV)
+
+
+@pytest.mark.parametrize("off", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("trans_rhs", [False, True])
+def test_every_window_offset(off, trans_rhs):
+    say(f"window off={off} trans_rhs={trans_rhs}")
+    gs_host = np.array([70, 0, 150, 5, 129, 0, 90], dtype=np.int32)
+    m, k, n, gl = int(gs_host.sum()) + 20, 136, 200, 3
+    x, w, gs = _case(m, k, n, gs_host, gl, 10 + off, trans_rhs)
+    o32, o16 = run_forward(x, w, gs, off=off, trans_rhs=trans_rhs)
+    check_forward_full(x, w, gs_host, off, None, trans_rhs, o32, o16, f"off={off}")
+
+
+@pytest.mark.parametrize("off", [-1, 5, 7, 1 << 30])
+def test_window_that_does_not_fit_is_all_zero(off):
+    say(f"invalid window off={off}")
+    gs_host = np.array([30, 40, 50, 60, 70, 80, 90], dtype=np.int32)
+    x, w, gs = _case(420, 64, 64, gs_host, 3, 3)
+    o32, o16 = run_forward(x, w, gs, off=off, limit=400)
+    assert bool(is_pos_zero(o32[:400]).all()) and bool(is_pos_zero(o16[:400]).all())
+    assert bool(is_sentinel(o32[400:]).all())
+    dw = sentinel((3, 64, 64), torch.float32)
+    rd.trans_ragged_dot(x, x, gs, num_local=3, group_offset=dev_i32(off), out=dw)
+    torch.cuda.synchronize()
+    assert bool(is_pos_zero(dw).all())
+
+
+@pytest.mark.parametrize("limit", [0, 1, 1023, 1259, 1262, 2253, 5000, -7])
+def test_limit_sweep_packed_buffer(limit):
+    """Page limit sweep scaled to a 2253-row packed buffer with NaN rows past the valid count."""
+    say(f"limit sweep limit={limit}")
+    gs_host = workloads.random_sizes(32, 1262, seed=5)
+    m, k, n = 2253, 128, 256
+    x, w, gs = _case(m, k, n, gs_host, 4, 21, nan_from=1262)
+    o32, o16 = run_forward(x, w, gs, off=12, limit=limit)
+    check_forward_full(x, w, gs_host, 12, limit, False, o32, o16, f"limit={limit}")
+    # trans: NaN rows past the limit (and outside groups) never reach dW
+    dy = bf16_normal((m, n), 1.0, 99, "cpu", nan_rows_from=1262).to(DEV)
+    dw = sentinel((4, k, n), torch.float32)
+    rd.trans_ragged_dot(x, dy, gs, num_local=4, group_offset=dev_i32(12), limit=dev_i32(limit), out=dw)
+    torch.cuda.synchronize()
+    ref = oracle.trans_ragged_dot(bits(x), bits(dy), gs_host, 4, 12, limit)
+    assert_gemm_close(dw.cpu().numpy(), ref, f"dW limit={limit}")
+
+
+@pytest.mark.parametrize("m,k,n,gs_list", [
+    (300, 200, 136, [37, 0, 129, 1, 133]),        # every dim ragged against the tiles
+    (5, 8, 8, [2, 0, 3]),                          # smaller than one tile
+    (1000, 64, 64, [0, 0, 0, 0]),                  # all groups empty
+    (100, 64, 72, [60, 70, 80]),                   # sizes sum past m: clamped at m
+    (200, 64, 64, [50, -20, 100, 30]),             # negative size counts as 0
+    (257, 1032, 264, [128, 129]),                  # exact tile edges
+])
+def test_ragged_tails_and_degenerate_sizes(m, k, n, gs_list):
+    say(f"tails m={m} k={k} n={n} gs={gs_list}")
+    gs_host = np.array(gs_list, dtype=np.int32)
+    G = len(gs_list)
+    for trans_rhs in (False, True):
+        x, w, gs = _case(m, k, n, gs_host, G, m + k, trans_rhs)
+        o32, o16 = run_forward(x, w, gs, trans_rhs=trans_rhs)
+        check_forward_full(x, w, gs_host, None, None, trans_rhs, o32, o16, f"tails trans_rhs={trans_rhs}")
+    dy = bf16_normal((m, n), 1.0, 5, "cpu").to(DEV)
+    dw = sentinel((G, k, n), torch.float32)
+    rd.trans_ragged_dot(x, dy, gs, out=dw)
+    torch.cuda.synchronize()
+    assert_gemm_close(dw.cpu().numpy(), oracle.trans_ragged_dot(bits(x), bits(dy), gs_host), "tails dW")
+
+
+def test_empty_rows_is_a_no_op():
+    say("m = 0")
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    w = torch.zeros((2, 64, 64), dtype=torch.bfloat16, device=DEV)
+    gs = torch.zeros(2, dtype=torch.int32, device=DEV)
+    out = rd.ragged_dot(x, w, gs)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 64)
+    dw = rd.trans_ragged_dot(x, x, gs)
+    torch.cuda.synchronize()
+    assert bool((dw == 0).all())
+
+
+def test_repeat_runs_are_bitwise_identical():
+    say("determinism")
+    gs_host = workloads.random_sizes(16, 3000, seed=8, empty=(3,))
+    x, w, gs = _case(3000, 512, 384, gs_host, 16, 40)
+    a = rd.ragged_dot(x, w, gs, out_dtype=torch.float32)
+    b = rd.ragged_dot(x, w, gs, out_dtype=torch.float32)
+    dy = bf16_normal((3000, 384), 1.0, 41, DEV)
+    c = rd.trans_ragged_dot(x, dy, gs)
+    d = rd.trans_ragged_dot(x, dy, gs)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert torch.equal(c.view(torch.int32), d.view(torch.int32))
+
+
+def test_windows_partition_the_full_result():
+    """Eight expert-parallel shards of 32 groups: window results add up to the full 256-group result."""
+    say("window partition")
+    G, gl, m, k, n = 256, 32, 4000, 128, 128
+    gs_host = workloads.random_sizes(G, 3900, seed=12)
+    x = bf16_normal((m, k), 1.0, 50, DEV)
+    w = bf16_normal((G, k, n), 0.05, 51, DEV)
+    gs = torch.from_numpy(gs_host).to(DEV)
+    full = rd.ragged_dot(x, w, gs, out_dtype=torch.float32)
+    acc = torch.zeros_like(full)
+    dws = []
+    dy = bf16_normal((m, n), 1.0, 52, DEV)
+    for s in range(G // gl):
+        part = rd.ragged_dot(x, w[s * gl:(s + 1) * gl].contiguous(), gs, group_offset=dev_i32(s * gl),
+                             out_dtype=torch.float32)
+        acc += part
+        dws.append(rd.trans_ragged_dot(x, dy, gs, num_local=gl, group_offset=dev_i32(s * gl)))
+    full_dw = rd.trans_ragged_dot(x, dy, gs)
+    torch.cuda.synchronize()
+    # each row is computed by exactly one shard with the same K order: bitwise equal
+    assert torch.equal(acc.view(torch.int32), full.view(torch.int32))
+    assert torch.equal(torch.cat(dws).view(torch.int32), full_dw.view(torch.int32))
+
+
+# ------------------------------------------------------------ full-size workloads, sampled rows
+
+def _sample_rows(lb, L, rng, per_group=2, extra=64):
+    rows = set()
+    for j in range(len(lb) - 1):
+        if lb[j + 1] > lb[j]:
+            rows.update({int(lb[j]), int(lb[j + 1]) - 1})
+            rows.update(int(r) for r in rng.integers(lb[j], lb[j + 1], size=per_group))
+    if L > 0:
+        rows.update(int(r) for r in rng.integers(0, L, size=extra))
+        rows.update({0, L - 1})
+    return np.array(sorted(r for r in rows if r < L), dtype=np.int64)
+
+
+def _check_sampled_forward(d, x, w, off, limit, o32, o16, trans_rhs, what, rng):
+    gs_host = d["gs_host"]
+    m = x.shape[0]
+    lb, lo, hi, L = oracle.boundaries(gs_host, m, off, w.shape[0], limit)
+    rows = _sample_rows(lb, L, rng)
+    # The oracle sees only the sampled rows: they are sorted, so their owners are
+    # non-decreasing and the per-owner counts are a valid group_sizes for them.
+    inside = (rows >= lo) & (rows < hi)
+    owner = np.searchsorted(lb, rows, side="right") - 1
+    rin = rows[inside]
+    counts = np.bincount(owner[inside], minlength=w.shape[0]).astype(np.int32)
+    ref = np.zeros((rows.size, o32.shape[1]))
+    if rin.size:
+        xs = bits(x[torch.from_numpy(rin).to(DEV)])
+        ref[inside] = oracle.ragged_dot(xs, bits(w), counts, trans_rhs=trans_rhs)
+    got = o32[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    assert_gemm_close(got, ref, what)
+    outside = torch.ones(L, dtype=torch.bool, device=DEV)
+    outside[lo:hi] = False
+    assert bool(is_pos_zero(o32[:L][outside]).all()), what
+    assert bool(is_sentinel(o32[L:]).all()) and bool(is_sentinel(o16[L:]).all()), what
+    assert_bf16_is_rne_of_f32(o16[:L], o32[:L], what)
+
+
+def test_full_moe_up_projection():
+    say("full workload: moe up-projection m8192 k4096 n2048 g64")
+    d = workloads.make(2, DEV)
+    o32, o16 = run_forward(d["x"], d["w"], d["gs"])
+    _check_sampled_forward(d, d["x"], d["w"], None, None, o32, o16, False, "up-proj", np.random.default_rng(2))
+
+
+def test_full_moe_up_projection_dw():
+    say("full workload: moe up-projection dW[64,4096,2048]")
+    d = workloads.make(2, DEV)
+    dw32 = rd.trans_ragged_dot(d["x"], d["dy"], d["gs"])
+    dw16 = rd.trans_ragged_dot(d["x"], d["dy"], d["gs"], out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    cols = [0, 1, 127, 128, 2049, 4095]
+    ref = oracle.trans_ragged_dot(bits(d["x"][:, cols].contiguous()), bits(d["dy"]), d["gs_host"])
+    assert_gemm_close(dw32[:, cols].cpu().numpy(), ref, "up-proj dW")
+    assert_bf16_is_rne_of_f32(dw16, dw32, "up-proj dW")
+
+
+def test_full_moe_backward():
+    say("full workload: moe backward dx (trans_rhs) and dW[64,1024,4096]")
+    d = workloads.make(3, DEV)
+    assert int(d["gs_host"].sum()) == 32768 and all(d["gs_host"][[0, 17, 18, 63]] == 0)
+    # dx = ragged_dot(dy, w, trans_rhs) with w [64, n_out=1024, k=4096]
+    o32, o16 = run_forward(d["dy"], d["w"], d["gs"], trans_rhs=True)
+    _check_sampled_forward(d, d["dy"], d["w"], None, None, o32, o16, True, "dx", np.random.default_rng(3))
+    dw32 = rd.trans_ragged_dot(d["x"], d["dy"], d["gs"])
+    torch.cuda.synchronize()
+    cols = [0, 5, 511, 512, 1023]
+    ref = oracle.trans_ragged_dot(bits(d["x"][:, cols].contiguous()), bits(d["dy"]), d["gs_host"])
+    assert_gemm_close(dw32[:, cols].cpu().numpy(), ref, "backward dW")
+    for j in (0, 17, 18, 63):
+        assert bool(is_pos_zero(dw32[j]).all()), f"empty group {j} dW not +0"
+
+
+def test_full_window_and_limit():
+    say("full workload: window off96 gl32 of 256, buffer 225280x4096, limit 126156")
+    d = workloads.make(4, DEV, parts=("x", "w"))
+    o32, o16 = run_forward(d["x"], d["w"], d["gs"], off=96, limit=126156)
+    _check_sampled_forward(d, d["x"], d["w"], 96, 126156, o32, o16, False, "window+limit",
+                           np.random.default_rng(4))
+
+
+def test_full_decode():
+    say("full workload: decode m512 k4096 n1536 g128")
+    d = workloads.make(5, DEV)
+    assert (d["gs_host"] == 0).sum() >= 38
+    o32, o16 = run_forward(d["x"], d["w"], d["gs"])
+    check_forward_full(d["x"], d["w"], d["gs_host"], None, None, False, o32, o16, "decode")
