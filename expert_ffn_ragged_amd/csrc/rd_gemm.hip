@@ -31,6 +31,7 @@
 //  * tiles are ordered so that consecutive logical tiles land on one XCD,
 //    which keeps a group's weight slab and rows in that XCD's L2.
 #include <cstdlib>
+#include <type_traits>
 
 #include "rd_device.h"
 #include "rd_launch.h"
@@ -63,10 +64,27 @@ struct KArgs {
 // lanes per phase, here 16 consecutive rows at one logical chunk; chunk c of
 // row r sits at slot c ^ ((r >> 1) & 7), so rows of equal parity (same bank
 // half) get 8 distinct slots and the 16 rows hit 16 distinct bank groups.
-struct KLayout {
-  __device__ __forceinline__ static int slot(int r, int c) { return c ^ ((r >> 1) & 7); }
-  __device__ __forceinline__ static int offset(int r, int c) { return r * BK + (slot(r, c) << 3); }
+//
+// With 32-element rows (64 bytes, four rows per bank line) the key is
+// c ^ ((r >> 2) & 3): rows with equal r % 4 share a bank quarter and get 4
+// distinct slots, so 16 consecutive rows again hit 16 distinct bank groups.
+template <int KS>
+struct KLayoutT {
+  static constexpr int kChunks = KS / 8;
+  static_assert(kChunks == 8 || kChunks == 4, "K-tile rows of 64 or 32 elements");
+  __device__ __forceinline__ static int slot(int r, int c) {
+    if constexpr (kChunks == 8) return c ^ ((r >> 1) & 7);
+    else return c ^ ((r >> 2) & 3);
+  }
+  __device__ __forceinline__ static int offset(int r, int c) { return r * KS + (slot(r, c) << 3); }
+  // MFMA fragment: lane l gets tile row (r_base + l % 32), contraction
+  // elements ks*16 + 8*(l/32) .. +7.
+  __device__ __forceinline__ static bf16x8_t frag(const uint16_t* tile, int r_base, int ks) {
+    const int l = threadIdx.x & 63;
+    return *reinterpret_cast<const bf16x8_t*>(tile + offset(r_base + (l & 31), 2 * ks + (l >> 5)));
+  }
 };
+using KLayout = KLayoutT<BK>;
 
 // MN-contiguous operand tile: BK rows (one per contraction index) of COLS
 // elements.  Chunk c of row r sits at slot c ^ swz(r), so the four rows one
@@ -201,63 +219,82 @@ __device__ __forceinline__ u32x4_t make_rsrc(const void* base, unsigned long lon
 // M0 holds the LDS base and needs one wait state before the load uses it.
 // M0 is a reserved register (never allocated; the compiler sets it right
 // before each instruction that reads it), so it is not listed as clobbered.
-__device__ __forceinline__ void dma16(u32x4_t r, uint16_t* lds, uint32_t voff, uint32_t soff) {
-  const uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(RD_LDS(void, lds)));
+__device__ __forceinline__ void dma16(u32x4_t r, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
-               : "s"(a), "v"(voff), "s"(r), "s"(soff)
+               : "s"(lds_addr), "v"(voff), "s"(r), "s"(soff)
                : "memory");
 }
 
-// K-contiguous operand fed by DMA.  The buffer starts at the tile's first row
-// and covers only its valid rows; tile row r is buffer row r, contraction
-// step kt covers columns [kt*BK, kt*BK + BK).  Each wave fills 1 KB slices
-// (8 rows) of the KLayout tile: lane i writes slot i % 8 of row i / 8, so it
-// fetches the logical chunk stored there, (i % 8) ^ ((row >> 1) & 7).
-template <int ROWS>
+// Scalar operands of dma16 are wave-uniform by construction; readfirstlane
+// states it, so the compiler keeps them in SGPRs as the instruction needs.
+__device__ __forceinline__ uint32_t uniform(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
+}
+__device__ __forceinline__ u32x4_t uniform(u32x4_t r) {
+  return u32x4_t{uniform(r[0]), uniform(r[1]), uniform(r[2]), uniform(r[3])};
+}
+
+// 32-bit LDS address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return uniform(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(RD_LDS(const void, p))));
+}
+
+// K-contiguous operand fed by DMA, KS contraction elements per stage.  The
+// buffer starts at the tile's first row and covers only its valid rows; tile
+// row r is buffer row r, stage kt covers columns [kt*KS, kt*KS + KS).  Each
+// wave fills 1 KB slices (64 / (KS/8) rows) of the KLayoutT<KS> tile: lane i
+// writes slot i % (KS/8) of its row, so it fetches the logical chunk stored
+// there (the slot map is an involution).
+template <int ROWS, int KS>
 struct KDma {
-  static constexpr int kInstr = ROWS / 32;  // 1 KB slices per wave per stage
+  static constexpr int kCh = KS / 8;
+  static constexpr int kRowsPerSlice = 64 / kCh;
+  static constexpr int kInstr = ROWS / kRowsPerSlice / 4;  // 1 KB slices per wave per stage
   static_assert(kInstr >= 1, "tile too small");
   u32x4_t rsrc;
   uint32_t voff[kInstr];
 
   __device__ __forceinline__ void init(const uint16_t* base, long long rows_valid, int ld, int wave) {
-    rsrc = make_rsrc(base, static_cast<unsigned long long>(rows_valid) * ld * 2);
+    rsrc = uniform(make_rsrc(base, static_cast<unsigned long long>(rows_valid) * ld * 2));
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int q = 0; q < kInstr; ++q) {
-      const int row = 8 * (wave * kInstr + q) + (lane >> 3);
-      const int c = KLayout::slot(row, lane & 7);  // the slot map is an involution
+      const int row = kRowsPerSlice * (wave * kInstr + q) + lane / kCh;
+      const int c = KLayoutT<KS>::slot(row, lane % kCh);
       voff[q] = static_cast<uint32_t>(row) * ld * 2 + c * 16;
     }
   }
-  __device__ __forceinline__ void issue(uint16_t* tile, int kt, int wave) const {
+  // tile: LDS byte address of this operand's stage buffer.
+  __device__ __forceinline__ void issue(uint32_t tile, int kt, int wave) const {
+    const uint32_t soff = uniform(kt * KS * 2);
 #pragma unroll
-    for (int q = 0; q < kInstr; ++q) dma16(rsrc, tile + (wave * kInstr + q) * 512, voff[q], kt * BK * 2);
+    for (int q = 0; q < kInstr; ++q) dma16(rsrc, tile + (wave * kInstr + q) * 1024, voff[q], soff);
   }
   __device__ __forceinline__ static bf16x8_t frag(const uint16_t* tile, int r_base, int ks) {
-    return KOperand<ROWS>::frag(tile, r_base, ks);
+    return KLayoutT<KS>::frag(tile, r_base, ks);
   }
 };
 
-// MN-contiguous operand fed by DMA.  The buffer starts at the first
-// contraction row and covers only valid rows; step kt covers rows
-// [kt*BK, kt*BK + BK), tile columns are [mn0, mn0 + COLS).  A 1 KB slice is
-// 512 / COLS rows of the MNLayout tile; lane i writes slot i % (COLS/8) of its
-// row and fetches logical chunk slot ^ swz(row).
-template <int COLS>
+// MN-contiguous operand fed by DMA, KS contraction rows per stage.  The
+// buffer starts at the first contraction row and covers only valid rows;
+// stage kt covers rows [kt*KS, kt*KS + KS), tile columns are
+// [mn0, mn0 + COLS).  A 1 KB slice is 512 / COLS rows of the MNLayout tile;
+// lane i writes slot i % (COLS/8) of its row and fetches logical chunk
+// slot ^ swz(row).
+template <int COLS, int KS>
 struct MNDma {
   static constexpr int kCpr = COLS / 8;
   static constexpr int kRowsPerSlice = 512 / COLS;
-  static constexpr int kInstr = COLS / 32;
+  static constexpr int kInstr = KS * COLS / 2048;
   static_assert(kInstr >= 1, "tile too small");
   u32x4_t rsrc;
   uint32_t voff[kInstr];
   uint32_t step_bytes;
 
   __device__ __forceinline__ void init(const uint16_t* base, long long rows_valid, int ld, int mn0, int wave) {
-    rsrc = make_rsrc(base, static_cast<unsigned long long>(rows_valid) * ld * 2);
-    step_bytes = static_cast<uint32_t>(BK) * ld * 2;
+    rsrc = uniform(make_rsrc(base, static_cast<unsigned long long>(rows_valid) * ld * 2));
+    step_bytes = uniform(static_cast<uint32_t>(KS) * ld * 2);
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int q = 0; q < kInstr; ++q) {
@@ -266,20 +303,22 @@ struct MNDma {
       voff[q] = static_cast<uint32_t>(row) * ld * 2 + (mn0 + c * 8) * 2;
     }
   }
-  __device__ __forceinline__ void issue(uint16_t* tile, int kt, int wave) const {
+  // tile: LDS byte address of this operand's stage buffer.
+  __device__ __forceinline__ void issue(uint32_t tile, int kt, int wave) const {
+    const uint32_t soff = uniform(kt * step_bytes);
 #pragma unroll
-    for (int q = 0; q < kInstr; ++q) dma16(rsrc, tile + (wave * kInstr + q) * 512, voff[q], kt * step_bytes);
+    for (int q = 0; q < kInstr; ++q) dma16(rsrc, tile + (wave * kInstr + q) * 1024, voff[q], soff);
   }
   __device__ __forceinline__ static bf16x8_t frag(const uint16_t* tile, int c_base, int ks) {
     return MNOperand<COLS>::frag(tile, c_base, ks);
   }
 };
 
-// MFMAs of one BK stage.  Fragments are double-buffered across the four
+// MFMAs of one KS-deep stage.  Fragments are double-buffered across its
 // 16-deep slices: slice ks+1 is read from LDS while slice ks multiplies, and a
 // scheduling fence per slice keeps at most two fragment sets live (with 256
 // accumulators per lane a deeper hoist would spill).
-template <class OpA, class OpB, int MI, int NI>
+template <class OpA, class OpB, int MI, int NI, int KS = BK>
 __device__ __forceinline__ void mma_stage(const uint16_t* ta, const uint16_t* tb, f32x16_t (&acc)[MI][NI],
                                           int wm_off, int wn_off) {
   bf16x8_t af[2][MI], bfr[2][NI];
@@ -288,9 +327,9 @@ __device__ __forceinline__ void mma_stage(const uint16_t* ta, const uint16_t* tb
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni) bfr[0][ni] = OpB::frag(tb, wn_off + ni * 32, 0);
 #pragma unroll
-  for (int ks = 0; ks < BK / 16; ++ks) {
+  for (int ks = 0; ks < KS / 16; ++ks) {
     const int cur = ks & 1;
-    if (ks + 1 < BK / 16) {
+    if (ks + 1 < KS / 16) {
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) af[cur ^ 1][mi] = OpA::frag(ta, wm_off + mi * 32, ks + 1);
 #pragma unroll
@@ -311,63 +350,19 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // Wait until at most `after` stages of this wave's loads remain in flight
-// (after in [0, S-2], uniform).  vmcnt needs an immediate, hence the ladder.
-template <int L, int S>
-__device__ __forceinline__ void wait_stages(int after) {
-  static_assert(S >= 2 && S <= 6 && (S - 2) * L <= 63, "pipeline depth");
-  if constexpr (S >= 6) {
-    if (after >= 4) { wait_vm<4 * L>(); return; }
-  }
-  if constexpr (S >= 5) {
-    if (after >= 3) { wait_vm<3 * L>(); return; }
-  }
-  if constexpr (S >= 4) {
-    if (after >= 2) { wait_vm<2 * L>(); return; }
-  }
-  if constexpr (S >= 3) {
-    if (after >= 1) { wait_vm<L>(); return; }
-  }
-  wait_vm<0>();
-}
-
-// acc += A_tile * B_tile over nk steps through an S-stage LDS ring fed by
-// buffer-to-LDS loads.  Step kt: wait for this wave's loads of stage kt,
-// barrier (every wave's loads of stage kt have landed and every wave is done
-// with step kt-1), refill the stage step kt-1 used with step kt+S-1, then
-// multiply stage kt.  The raw s_barrier keeps later stages in flight across
-// it (a __syncthreads fence would drain them).  Ends with a barrier so the
-// next tile may refill any stage.
-template <class OpA, class OpB, int MI, int NI, int S, int A_EL, int B_EL>
-__device__ __forceinline__ void k_loop_dma(const OpA& A, const OpB& B, int nk, uint16_t* s_tiles,
-                                           f32x16_t (&acc)[MI][NI], int wm_off, int wn_off, int wave) {
-  if (nk <= 0) return;
-  constexpr int L = OpA::kInstr + OpB::kInstr;  // loads per wave per stage
-  constexpr int ST = A_EL + B_EL;
-#pragma unroll
-  for (int s = 0; s < S - 1; ++s) {
-    if (s < nk) {
-      A.issue(s_tiles + s * ST, s, wave);
-      B.issue(s_tiles + s * ST + A_EL, s, wave);
+// (after in [0, K], uniform); vmcnt takes an immediate, hence the ladder.
+template <int L, int K>
+__device__ __forceinline__ void wait_ladder(int after) {
+  static_assert(K * L <= 63, "vmcnt counts up to 63 operations");
+  if constexpr (K > 0) {
+    if (after >= K) {
+      wait_vm<K * L>();
+      return;
     }
+    wait_ladder<L, K - 1>(after);
+  } else {
+    wait_vm<0>();
   }
-  for (int kt = 0; kt < nk; ++kt) {
-    const int after = min(nk - 1 - kt, S - 2);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_stages<L, S>(after);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    const int nxt = kt + S - 1;
-    if (nxt < nk) {
-      const int s = nxt % S;
-      A.issue(s_tiles + s * ST, nxt, wave);
-      B.issue(s_tiles + s * ST + A_EL, nxt, wave);
-    }
-    const int cur = kt % S;
-    mma_stage<OpA, OpB, MI, NI>(s_tiles + cur * ST, s_tiles + cur * ST + A_EL, acc, wm_off, wn_off);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
 }
 
 // ---------------------------------------------------------------- tile main loop
@@ -434,78 +429,321 @@ __device__ __forceinline__ void store_block(const f32x16_t& acc, void* out, bool
   }
 }
 
-// Store a wave's (MI*32) x (NI*32) accumulator block at out[r0.., c0..].
-// float32 goes out directly (32 lanes cover 128 contiguous bytes of a row).
-// bf16 is rounded and staged through this wave's private LDS area as the
-// transposed block T[col][row] (4 consecutive rows per 8-byte write); the LDS
-// transpose read then hands each lane 4 + 4 consecutive columns of one row,
-// so the block leaves in 16-byte stores.  Only this wave touches `stage`.
+// Epilogue staging: 16 rows x 32 floats per wave at a time, row-major, rows
+// padded to 36 floats (144 bytes: consecutive rows start in distinct 16-byte
+// bank slots).
+constexpr int kStagePitch = 36;
+constexpr int kStageFloats = 16 * kStagePitch;  // per wave
+
+// Store a wave's (MI*32) x (NI*32) accumulator block at out[r0.., c0..]
+// (row pitch ld elements, rows < rlim, columns < clim).  Each 32 x 32 block
+// goes through this wave's private LDS area in two 16-row halves: the
+// accumulators are written straight from their registers (MFMA layout: lane
+// l holds column l % 32 of rows 8*(v/4) + 4*(l/32) + v%4; half h takes v/4 in
+// {2h, 2h+1}), so 32 lanes fill 128 contiguous bytes of a row per write;
+// then every lane reads 8 consecutive floats of one row, rounds them (bf16,
+// round-to-nearest-even) or keeps them (f32), and issues 16-byte stores.  No
+// accumulator is copied into general registers wholesale, which keeps
+// 256-accumulator tiles unspilled.  LDS operations of one wave run in order,
+// so the area is reused safely.
 template <int MI, int NI>
 __device__ __forceinline__ void store_wave_tile(const f32x16_t (&acc)[MI][NI], void* out, bool f32, long long ld,
-                                                int r0, int rlim, int c0, int clim, uint16_t* stage) {
-  constexpr int WM = MI * 32, WN = NI * 32;
-  // Fences per 32-row block keep at most NI accumulator blocks in VGPRs at a time.
-  if (f32) {
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) store_block(acc[mi][ni], out, true, ld, r0 + mi * 32, rlim, c0 + ni * 32, clim);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    return;
-  }
-  using T = MNLayout<WM>;
+                                                int r0, int rlim, int c0, int clim, float* stage) {
   const int l = threadIdx.x & 63;
+  const int rr = l >> 2, cc = (l & 3) * 8;  // read-back: row rr of the half, columns cc .. cc+7
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi) {
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int col = ni * 32 + (l & 31);
-        const int row = mi * 32 + 8 * i + 4 * (l >> 5);
-        const uint2 v = make_uint2(pack_bf16x2(acc[mi][ni][4 * i], acc[mi][ni][4 * i + 1]),
-                                   pack_bf16x2(acc[mi][ni][4 * i + 2], acc[mi][ni][4 * i + 3]));
-        *reinterpret_cast<uint2*>(stage + T::offset(col, row >> 3) + (row & 7)) = v;
-      }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  const int g = l >> 4, q = l & 15;
-  uint16_t* o = static_cast<uint16_t*>(out);
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
-  for (int rb = 0; rb < WM / 16; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < WN / 32; ++cb) {
-      const int rl = rb * 16, cl = cb * 32 + 8 * g;
-      const int tcol = rl + 4 * (q & 3);
-      const uint16_t* p0 = stage + T::offset(cl + (q >> 2), tcol >> 3) + (tcol & 7);
-      const uint16_t* p1 = stage + T::offset(cl + 4 + (q >> 2), tcol >> 3) + (tcol & 7);
-      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(RD_LDS(s16x4_t, p0));
-      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(RD_LDS(s16x4_t, p1));
-      const int grow = r0 + rl + q, gcol = c0 + cl;
-      if (grow < rlim && gcol < clim) {
-        typedef short s16x8_t __attribute__((ext_vector_type(8)));
-        const s16x8_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        *reinterpret_cast<s16x8_t*>(o + grow * ld + gcol) = both;
+        for (int v = 8 * h; v < 8 * h + 8; ++v)
+          stage[(8 * (v >> 2) - 16 * h + 4 * (l >> 5) + (v & 3)) * kStagePitch + (l & 31)] = acc[mi][ni][v];
+        const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(stage + rr * kStagePitch + cc);
+        const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(stage + rr * kStagePitch + cc + 4);
+        const int grow = r0 + mi * 32 + 16 * h + rr, gcol = c0 + ni * 32 + cc;
+        if (grow < rlim && gcol < clim) {
+          if (f32) {
+            float* o = static_cast<float*>(out) + grow * ld + gcol;
+            *reinterpret_cast<f32x4_t*>(o) = lo;
+            *reinterpret_cast<f32x4_t*>(o + 4) = hi;
+          } else {
+            const uint4 v = make_uint4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
+                                       pack_bf16x2(hi[2], hi[3]));
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + grow * ld + gcol) = v;
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
 }
 
-// ---------------------------------------------------------------- kernels
+// Zeros for a wave's block (a local group with no rows gets an all +0 dW).
+template <int MI, int NI>
+__device__ __forceinline__ void store_wave_zero(void* out, bool f32, long long ld, int r0, int rlim, int c0,
+                                                int clim) {
+  constexpr int WM = MI * 32, WN = NI * 32;
+  const int esz = f32 ? 4 : 2;
+  const int cpr = WN * esz / 16;  // 16-byte chunks per row of the block
+  const int l = threadIdx.x & 63;
+  for (int i = l; i < WM * cpr; i += 64) {
+    const int r = r0 + i / cpr, c = c0 + (i % cpr) * (16 / esz);
+    if (r < rlim && c < clim)
+      *reinterpret_cast<uint4*>(static_cast<char*>(out) + (r * ld + c) * esz) = make_uint4(0, 0, 0, 0);
+  }
+}
 
-// STAGES > 0: buffer-to-LDS pipeline with that many LDS stages (one workgroup
-// per CU); STAGES == 0: register-staged fallback (two workgroups per CU).
-// Occupancy: the register-staged and the 2-stage 128x128 variants run two
-// workgroups per CU (their LDS fits twice), every other shape one.
-template <int MODE, int BM, int BN, int STAGES>
-__global__ __launch_bounds__(kThreads, (STAGES == 0 || (STAGES == 2 && BM * BN <= 128 * 128)) ? 2 : 1)
-void grouped_gemm_kernel(KArgs p) {
+// ---------------------------------------------------------------- tile lists
+
+// Forward tiles: local group j owns ceil(rows_j / BM) m-tiles, each with
+// n_tiles n-tiles.  Within a group, tiles come in blocks of gm m-tiles x all
+// n-tiles (m-tile fastest), gm sized so one block roughly fills the
+// workgroups of one XCD: tiles running together share each row block of x
+// across the n-tiles and each weight slice across gm m-tiles.  Logical tiles
+// are dealt so that consecutive ones land on one XCD.
+struct FwdTiles {
+  long long T, per_xcd, slots;
+  int n_tiles, gm;
+  struct Tile {
+    int j, row0, row_end, n0, nk;
+  };
+  __device__ __forceinline__ void init(int total_m, int n, int BN, int k) {
+    n_tiles = (n + BN - 1) / BN;
+    T = static_cast<long long>(total_m) * n_tiles;
+    per_xcd = (T + kXcds - 1) / kXcds;
+    slots = per_xcd * kXcds;
+    gm = max(1, max(1, static_cast<int>(gridDim.x) / kXcds) / n_tiles);
+    (void)k;
+  }
+  template <int BM, int BN, int KS = BK>
+  __device__ __forceinline__ bool get(long long s, const int* s_lb, const int* s_aux, int gl, int k, Tile& t) const {
+    const long long lt = xcd_logical(s, per_xcd);
+    if (lt >= T) return false;
+    const int j = upper_index(s_aux, gl, static_cast<int>(lt / n_tiles));
+    const int mj = s_aux[j + 1] - s_aux[j];
+    const int within = static_cast<int>(lt - static_cast<long long>(s_aux[j]) * n_tiles);
+    const int mb = within / (gm * n_tiles);  // m-block of this group
+    const int rem = within - mb * gm * n_tiles;
+    const int bm = min(gm, mj - mb * gm);     // m-tiles in this (possibly short) block
+    const int nt = rem / bm, mt = mb * gm + (rem - nt * bm);
+    t.j = j;
+    t.row0 = s_lb[j] + mt * BM;
+    t.row_end = s_lb[j + 1];
+    t.n0 = nt * BN;
+    t.nk = (k + KS - 1) / KS;
+    return true;
+  }
+};
+
+// trans_ragged_dot tiles: every local group owns ka x nc output tiles of
+// dW[j]; the contraction runs over the group's rows.  Groups are visited
+// largest first (s_order); each XCD owns a contiguous slice of the n-tiles,
+// so it streams only its slice of dy while every XCD reads the narrower x.
+struct TransTiles {
+  long long per_x, slots;
+  int ka, nc, ncx;
+  bool split;
+  struct Tile {
+    int j, r_begin, r_end, a0, c0, nk;
+  };
+  __device__ __forceinline__ void init(int gl, int k, int n, int BM, int BN) {
+    ka = (k + BM - 1) / BM;
+    nc = (n + BN - 1) / BN;
+    split = nc >= kXcds;
+    ncx = split ? (nc + kXcds - 1) / kXcds : nc;
+    per_x = static_cast<long long>(gl) * ka * ncx;
+    slots = split ? per_x * kXcds : per_x;
+  }
+  template <int BM, int BN, int KS = BK>
+  __device__ __forceinline__ bool get(long long s, const int* s_lb, const int* s_order, Tile& t) const {
+    int x = 0;
+    long long i = s;
+    if (split) {
+      x = static_cast<int>(s % kXcds);
+      i = s / kXcds;
+    }
+    const int q = static_cast<int>(i / (static_cast<long long>(ka) * ncx));
+    const int rem = static_cast<int>(i - static_cast<long long>(q) * ka * ncx);
+    const int at = rem / ncx;
+    const int ct = x * ncx + (rem - at * ncx);
+    if (ct >= nc) return false;
+    t.j = s_order[q];
+    t.r_begin = s_lb[t.j];
+    t.r_end = s_lb[t.j + 1];
+    t.a0 = at * BM;
+    t.c0 = ct * BN;
+    t.nk = (t.r_end - t.r_begin + KS - 1) / KS;
+    return true;
+  }
+};
+
+// Groups of the window, largest first (stable), into s_order; plain order
+// when there are more than kThreads local groups.  Ends with a barrier.
+__device__ __forceinline__ void order_groups(const int* s_lb, int gl, int* s_order) {
+  if (gl <= kThreads) {
+    const int t = threadIdx.x;
+    if (t < gl) {
+      const int sz = s_lb[t + 1] - s_lb[t];
+      int rank = 0;
+      for (int i = 0; i < gl; ++i) {
+        const int si = s_lb[i + 1] - s_lb[i];
+        rank += (si > sz) || (si == sz && i < t);
+      }
+      s_order[rank] = t;
+    }
+  } else {
+    for (int t = threadIdx.x; t < gl; t += kThreads) s_order[t] = t;
+  }
+  __syncthreads();
+}
+
+// Rows below L outside the window are written as +0 (rows >= L untouched),
+// in tasks of kZeroRows rows shared by the whole grid.
+__device__ __forceinline__ void zero_outside_window(const KArgs& p, const Window& win) {
+  const int z1 = (win.lo + kZeroRows - 1) / kZeroRows;
+  const int z2 = (win.L - win.hi + kZeroRows - 1) / kZeroRows;
+  const int esz = p.out_f32 ? 4 : 2;
+  const int cpr = p.n * esz / 16;
+  for (int z = blockIdx.x; z < z1 + z2; z += gridDim.x) {
+    int r0, r1;
+    if (z < z1) {
+      r0 = z * kZeroRows;
+      r1 = min(r0 + kZeroRows, win.lo);
+    } else {
+      r0 = win.hi + (z - z1) * kZeroRows;
+      r1 = min(r0 + kZeroRows, win.L);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(p.out) + static_cast<long long>(r0) * p.n * esz);
+    const int nch = (r1 - r0) * cpr;
+    for (int q = threadIdx.x; q < nch; q += kThreads) dst[q] = make_uint4(0, 0, 0, 0);
+  }
+}
+
+// ---------------------------------------------------------------- register-staged kernel (fallback)
+
+// Two workgroups per CU; the contraction length may be any multiple of 8 and
+// operands may exceed 4 GiB.  Tiles run one after another, each with its own
+// double-buffered pipeline.
+template <int MODE, int BM, int BN>
+__global__ __launch_bounds__(kThreads, 2) void grouped_gemm_regs(KArgs p) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int MI = WM / 32, NI = WN / 32;
   constexpr int A_EL = BM * BK, B_EL = BN * BK;
-  constexpr int NBUF = STAGES > 0 ? STAGES : 2;
-  __shared__ __attribute__((aligned(1024))) uint16_t s_tiles[NBUF * (A_EL + B_EL)];
-  static_assert(4 * WM * WN <= NBUF * (A_EL + B_EL), "epilogue staging must fit in the pipeline ring");
+  __shared__ __attribute__((aligned(1024))) uint16_t s_tiles[2 * (A_EL + B_EL)];
+  static_assert(4 * kStageFloats * 2 <= 2 * (A_EL + B_EL), "epilogue staging must fit");
+  __shared__ int s_lb[RD_MAX_GROUPS + 1];
+  __shared__ int s_aux[RD_MAX_GROUPS + 1];
+  __shared__ long long s_wave[kThreads / 64];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm_off = (wave >> 1) * WM, wn_off = (wave & 1) * WN;
+  float* stage = reinterpret_cast<float*>(s_tiles) + wave * kStageFloats;
+  const Window win = build_local_bounds(p.gs, p.G, p.offp, p.gl, p.limp, p.m, s_lb, s_wave);
+
+  if constexpr (MODE == kFwdNN || MODE == kFwdNT) {
+    const int total_m = tile_prefix(s_lb, p.gl, BM, s_aux, s_wave);
+    FwdTiles tl;
+    tl.init(total_m, p.n, BN, p.k);
+    for (long long s = blockIdx.x; s < tl.slots; s += gridDim.x) {
+      FwdTiles::Tile t;
+      if (!tl.get<BM, BN>(s, s_lb, s_aux, p.gl, p.k, t)) continue;
+      const uint16_t* wj = p.b + static_cast<long long>(t.j) * p.k * p.n;
+      f32x16_t acc[MI][NI];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x16_t{};
+      KOperand<BM> A{p.a, p.k, t.row0, t.row_end, p.k};
+      if constexpr (MODE == kFwdNN) {
+        MNOperand<BN> B{wj, p.n, 0, p.k, t.n0, p.n};
+        k_loop<KOperand<BM>, MNOperand<BN>, MI, NI, A_EL, B_EL>(A, B, t.nk, s_tiles, acc, wm_off, wn_off);
+      } else {
+        KOperand<BN> B{wj, p.k, t.n0, p.n, p.k};
+        k_loop<KOperand<BM>, KOperand<BN>, MI, NI, A_EL, B_EL>(A, B, t.nk, s_tiles, acc, wm_off, wn_off);
+      }
+      store_wave_tile<MI, NI>(acc, p.out, p.out_f32, p.n, t.row0 + wm_off, t.row_end, t.n0 + wn_off, p.n, stage);
+      __syncthreads();  // staging area = pipeline buffers: drain before the next tile refills them
+    }
+    zero_outside_window(p, win);
+  } else {
+    order_groups(s_lb, p.gl, s_aux);
+    TransTiles tl;
+    tl.init(p.gl, p.k, p.n, BM, BN);
+    for (long long s = blockIdx.x; s < tl.slots; s += gridDim.x) {
+      TransTiles::Tile t;
+      if (!tl.get<BM, BN>(s, s_lb, s_aux, t)) continue;
+      f32x16_t acc[MI][NI];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x16_t{};
+      MNOperand<BM> A{p.a, p.k, t.r_begin, t.r_end, t.a0, p.k};
+      MNOperand<BN> B{p.b, p.n, t.r_begin, t.r_end, t.c0, p.n};
+      k_loop<MNOperand<BM>, MNOperand<BN>, MI, NI, A_EL, B_EL>(A, B, t.nk, s_tiles, acc, wm_off, wn_off);
+      char* dwj = static_cast<char*>(p.out) + static_cast<long long>(t.j) * p.k * p.n * (p.out_f32 ? 4 : 2);
+      store_wave_tile<MI, NI>(acc, dwj, p.out_f32, p.n, t.a0 + wm_off, p.k, t.c0 + wn_off, p.n, stage);
+      __syncthreads();
+    }
+  }
+}
+
+// ---------------------------------------------------------------- streamed buffer-to-LDS kernel
+
+// Operands of one tile, per mode.
+template <int MODE, int BM, int BN, int KS>
+struct StreamOps;
+template <int BM, int BN, int KS>
+struct StreamOps<kFwdNN, BM, BN, KS> {
+  using A = KDma<BM, KS>;
+  using B = MNDma<BN, KS>;
+  __device__ __forceinline__ static void make(const KArgs& p, const FwdTiles::Tile& t, int wave, A& a, B& b) {
+    a.init(p.a + static_cast<long long>(t.row0) * p.k, t.row_end - t.row0, p.k, wave);
+    b.init(p.b + static_cast<long long>(t.j) * p.k * p.n, p.k, p.n, t.n0, wave);
+  }
+};
+template <int BM, int BN, int KS>
+struct StreamOps<kFwdNT, BM, BN, KS> {
+  using A = KDma<BM, KS>;
+  using B = KDma<BN, KS>;
+  __device__ __forceinline__ static void make(const KArgs& p, const FwdTiles::Tile& t, int wave, A& a, B& b) {
+    a.init(p.a + static_cast<long long>(t.row0) * p.k, t.row_end - t.row0, p.k, wave);
+    b.init(p.b + static_cast<long long>(t.j) * p.k * p.n + static_cast<long long>(t.n0) * p.k, p.n - t.n0, p.k,
+           wave);
+  }
+};
+template <int BM, int BN, int KS>
+struct StreamOps<kTransTN, BM, BN, KS> {
+  using A = MNDma<BM, KS>;
+  using B = MNDma<BN, KS>;
+  __device__ __forceinline__ static void make(const KArgs& p, const TransTiles::Tile& t, int wave, A& a, B& b) {
+    a.init(p.a + static_cast<long long>(t.r_begin) * p.k, t.r_end - t.r_begin, p.k, t.a0, wave);
+    b.init(p.b + static_cast<long long>(t.r_begin) * p.n, t.r_end - t.r_begin, p.n, t.c0, wave);
+  }
+};
+
+// One persistent stream of contraction steps across all of a workgroup's
+// tiles.  A producer walks the workgroup's tile list issuing buffer-to-LDS
+// loads S-1 steps ahead of the consumer, crossing tile boundaries, so the
+// next tile's first stages load while the current tile multiplies and its
+// epilogue stores drain.  Step g lives in ring slot g % S.  Before step g the
+// wave waits until at most (younger loads) vector-memory operations are in
+// flight: loads complete in issue order, so step g's loads are then done
+// whatever the pending stores do.  The barrier that follows also tells every
+// wave that slot (g-1) % S is free, and the producer refills it.  A tile's
+// epilogue stages its bf16 results in the slot of its last step.
+// WGS workgroups share a CU (1, or 2 for the small-ring variant).
+template <int MODE, int BM, int BN, int S, int KS, int WGS>
+__global__ __launch_bounds__(kThreads, WGS) void grouped_gemm_stream(KArgs p) {
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int MI = WM / 32, NI = WN / 32;
+  constexpr int A_EL = BM * KS, B_EL = BN * KS, ST = A_EL + B_EL;
+  static_assert(4 * kStageFloats * 2 <= ST, "epilogue staging must fit in one ring slot");
+  using Ops = StreamOps<MODE, BM, BN, KS>;
+  using OpA = typename Ops::A;
+  using OpB = typename Ops::B;
+  using Tiles = typename std::conditional<MODE == kTransTN, TransTiles, FwdTiles>::type;
+  constexpr int L = OpA::kInstr + OpB::kInstr;  // loads per wave per step
+  __shared__ __attribute__((aligned(1024))) uint16_t s_tiles[S * ST];
   __shared__ int s_lb[RD_MAX_GROUPS + 1];
   __shared__ int s_aux[RD_MAX_GROUPS + 1];
   __shared__ long long s_wave[kThreads / 64];
@@ -514,140 +752,98 @@ void grouped_gemm_kernel(KArgs p) {
   const int wm_off = (wave >> 1) * WM, wn_off = (wave & 1) * WN;
   const Window win = build_local_bounds(p.gs, p.G, p.offp, p.gl, p.limp, p.m, s_lb, s_wave);
 
-  if constexpr (MODE == kFwdNN || MODE == kFwdNT) {
-    // Tiles: local group j owns ceil(rows_j / BM) m-tiles, each with n_tiles
-    // n-tiles; logical order (group, n-tile, m-tile).
-    const int total_m = tile_prefix(s_lb, p.gl, BM, s_aux, s_wave);
-    const int n_tiles = (p.n + BN - 1) / BN;
-    const long long T = static_cast<long long>(total_m) * n_tiles;
-    const long long per_xcd = (T + kXcds - 1) / kXcds;
-    for (long long s = blockIdx.x; s < per_xcd * kXcds; s += gridDim.x) {
-      const long long lt = xcd_logical(s, per_xcd);
-      if (lt >= T) continue;
-      const int j = upper_index(s_aux, p.gl, static_cast<int>(lt / n_tiles));
-      const int mj = s_aux[j + 1] - s_aux[j];
-      const int within = static_cast<int>(lt - static_cast<long long>(s_aux[j]) * n_tiles);
-      const int nt = within / mj, mt = within - nt * mj;
-      const int row0 = s_lb[j] + mt * BM, row_end = s_lb[j + 1];
-      const int n0 = nt * BN;
-      const uint16_t* wj = p.b + static_cast<long long>(j) * p.k * p.n;
-      f32x16_t acc[MI][NI];
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x16_t{};
-      const int nk = (p.k + BK - 1) / BK;
-      if constexpr (STAGES > 0) {
-        KDma<BM> A;
-        A.init(p.a + static_cast<long long>(row0) * p.k, row_end - row0, p.k, wave);
-        if constexpr (MODE == kFwdNN) {
-          MNDma<BN> B;
-          B.init(wj, p.k, p.n, n0, wave);
-          k_loop_dma<KDma<BM>, MNDma<BN>, MI, NI, STAGES, A_EL, B_EL>(A, B, nk, s_tiles, acc, wm_off, wn_off,
-                                                                       wave);
-        } else {
-          KDma<BN> B;
-          B.init(wj + static_cast<long long>(n0) * p.k, p.n - n0, p.k, wave);
-          k_loop_dma<KDma<BM>, KDma<BN>, MI, NI, STAGES, A_EL, B_EL>(A, B, nk, s_tiles, acc, wm_off, wn_off,
-                                                                      wave);
-        }
-      } else {
-        KOperand<BM> A{p.a, p.k, row0, row_end, p.k};
-        if constexpr (MODE == kFwdNN) {
-          MNOperand<BN> B{wj, p.n, 0, p.k, n0, p.n};
-          k_loop<KOperand<BM>, MNOperand<BN>, MI, NI, A_EL, B_EL>(A, B, nk, s_tiles, acc, wm_off, wn_off);
-        } else {
-          KOperand<BN> B{wj, p.k, n0, p.n, p.k};
-          k_loop<KOperand<BM>, KOperand<BN>, MI, NI, A_EL, B_EL>(A, B, nk, s_tiles, acc, wm_off, wn_off);
-        }
-      }
-      store_wave_tile<MI, NI>(acc, p.out, p.out_f32, p.n, row0 + wm_off, row_end, n0 + wn_off, p.n,
-                              s_tiles + wave * (WM * WN));
-      __syncthreads();  // staging area = pipeline ring: drain before the next tile refills it
-    }
-    // Rows below L outside the window are written as +0; rows >= L are untouched.
-    const int z1 = (win.lo + kZeroRows - 1) / kZeroRows;
-    const int z2 = (win.L - win.hi + kZeroRows - 1) / kZeroRows;
-    const int esz = p.out_f32 ? 4 : 2;
-    const int cpr = p.n * esz / 16;
-    for (int z = blockIdx.x; z < z1 + z2; z += gridDim.x) {
-      int r0, r1;
-      if (z < z1) {
-        r0 = z * kZeroRows;
-        r1 = min(r0 + kZeroRows, win.lo);
-      } else {
-        r0 = win.hi + (z - z1) * kZeroRows;
-        r1 = min(r0 + kZeroRows, win.L);
-      }
-      uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(p.out) + static_cast<long long>(r0) * p.n * esz);
-      const int nch = (r1 - r0) * cpr;
-      for (int q = threadIdx.x; q < nch; q += kThreads) dst[q] = make_uint4(0, 0, 0, 0);
-    }
+  Tiles tl;
+  if constexpr (MODE == kTransTN) {
+    order_groups(s_lb, p.gl, s_aux);
+    tl.init(p.gl, p.k, p.n, BM, BN);
   } else {
-    // trans_ragged_dot: every local group owns ka x nc output tiles of dW[j];
-    // the contraction runs over the group's rows.  Groups are visited largest
-    // first; each XCD owns a contiguous slice of the n-tiles, so it streams
-    // only its slice of dy while every XCD reads the (narrower) x rows.
-    const int gl = p.gl;
-    if (gl <= kThreads) {
-      const int t = threadIdx.x;
-      if (t < gl) {
-        const int sz = s_lb[t + 1] - s_lb[t];
-        int rank = 0;
-        for (int i = 0; i < gl; ++i) {
-          const int si = s_lb[i + 1] - s_lb[i];
-          rank += (si > sz) || (si == sz && i < t);
-        }
-        s_aux[rank] = t;
-      }
-    } else {
-      for (int t = threadIdx.x; t < gl; t += kThreads) s_aux[t] = t;
-    }
-    __syncthreads();
-    const int ka = (p.k + BM - 1) / BM;
-    const int nc = (p.n + BN - 1) / BN;
-    const bool split = nc >= kXcds;
-    const int ncx = split ? (nc + kXcds - 1) / kXcds : nc;
-    const long long per_x = static_cast<long long>(gl) * ka * ncx;  // tiles per XCD slice
-    const long long slots = split ? per_x * kXcds : per_x;
-    for (long long s = blockIdx.x; s < slots; s += gridDim.x) {
-      int x = 0;
-      long long i = s;
-      if (split) {
-        x = static_cast<int>(s % kXcds);
-        i = s / kXcds;
-      }
-      const int q = static_cast<int>(i / (static_cast<long long>(ka) * ncx));
-      const int rem = static_cast<int>(i - static_cast<long long>(q) * ka * ncx);
-      const int at = rem / ncx;
-      const int ct = x * ncx + (rem - at * ncx);
-      if (ct >= nc) continue;
-      const int j = s_aux[q];
-      const int r_begin = s_lb[j], r_end = s_lb[j + 1];
-      const int a0 = at * BM, c0 = ct * BN;
-      f32x16_t acc[MI][NI];
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x16_t{};
-      const int nk = (r_end - r_begin + BK - 1) / BK;
-      if constexpr (STAGES > 0) {
-        MNDma<BM> A;
-        A.init(p.a + static_cast<long long>(r_begin) * p.k, r_end - r_begin, p.k, a0, wave);
-        MNDma<BN> B;
-        B.init(p.b + static_cast<long long>(r_begin) * p.n, r_end - r_begin, p.n, c0, wave);
-        k_loop_dma<MNDma<BM>, MNDma<BN>, MI, NI, STAGES, A_EL, B_EL>(A, B, nk, s_tiles, acc, wm_off, wn_off, wave);
-      } else {
-        MNOperand<BM> A{p.a, p.k, r_begin, r_end, a0, p.k};
-        MNOperand<BN> B{p.b, p.n, r_begin, r_end, c0, p.n};
-        k_loop<MNOperand<BM>, MNOperand<BN>, MI, NI, A_EL, B_EL>(A, B, nk, s_tiles, acc, wm_off, wn_off);
-      }
-      char* dwj = static_cast<char*>(p.out) + static_cast<long long>(j) * p.k * p.n * (p.out_f32 ? 4 : 2);
-      store_wave_tile<MI, NI>(acc, dwj, p.out_f32, p.n, a0 + wm_off, p.k, c0 + wn_off, p.n,
-                              s_tiles + wave * (WM * WN));
-      __syncthreads();  // staging area = pipeline ring: drain before the next tile refills it
-    }
+    const int total_m = tile_prefix(s_lb, p.gl, BM, s_aux, s_wave);
+    tl.init(total_m, p.n, BN, p.k);
   }
+  auto tile_at = [&](long long s, typename Tiles::Tile& t) -> bool {
+    if constexpr (MODE == kTransTN)
+      return tl.template get<BM, BN, KS>(s, s_lb, s_aux, t);
+    else
+      return tl.template get<BM, BN, KS>(s, s_lb, s_aux, p.gl, p.k, t);
+  };
+  const uint32_t ring = lds_address(s_tiles);
+  const long long stride = gridDim.x;
+
+  // producer state: its tile (slot ps), operands, next step
+  long long ps = static_cast<long long>(blockIdx.x) - stride;
+  int p_kt = 0, p_nk = 0;
+  bool p_done = false;
+  OpA pa;
+  OpB pb;
+  int issued = 0;
+  auto produce = [&]() {
+    while (!p_done && p_kt >= p_nk) {
+      ps += stride;
+      if (ps >= tl.slots) {
+        p_done = true;
+        break;
+      }
+      typename Tiles::Tile t;
+      if (tile_at(ps, t) && t.nk > 0) {
+        Ops::make(p, t, wave, pa, pb);
+        p_kt = 0;
+        p_nk = t.nk;
+      }
+    }
+    if (p_done) return;
+    const uint32_t slot = ring + 2 * (issued % S) * ST;
+    pa.issue(slot, p_kt, wave);
+    pb.issue(slot + 2 * A_EL, p_kt, wave);
+    ++p_kt;
+    ++issued;
+  };
+
+#pragma unroll
+  for (int i = 0; i < S - 1; ++i) produce();
+
+  int g = 0;  // consumer step
+  for (long long cs = blockIdx.x; cs < tl.slots; cs += stride) {
+    typename Tiles::Tile t;
+    if (!tile_at(cs, t)) continue;
+    char* out;
+    int r0, rlim, c0;
+    if constexpr (MODE == kTransTN) {
+      out = static_cast<char*>(p.out) + static_cast<long long>(t.j) * p.k * p.n * (p.out_f32 ? 4 : 2);
+      r0 = t.a0 + wm_off;
+      rlim = p.k;
+      c0 = t.c0 + wn_off;
+    } else {
+      out = static_cast<char*>(p.out);
+      r0 = t.row0 + wm_off;
+      rlim = t.row_end;
+      c0 = t.n0 + wn_off;
+    }
+    if (t.nk == 0) {  // a local group with no rows: its dW tile is +0
+      store_wave_zero<MI, NI>(out, p.out_f32, p.n, r0, rlim, c0, p.n);
+      continue;
+    }
+    f32x16_t acc[MI][NI];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x16_t{};
+    for (int kt = 0; kt < t.nk; ++kt) {
+      __builtin_amdgcn_sched_barrier(0);
+      wait_ladder<L, S - 2>(issued - 1 - g);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      produce();
+      const uint16_t* slot = s_tiles + (g % S) * ST;
+      mma_stage<OpA, OpB, MI, NI, KS>(slot, slot + A_EL, acc, wm_off, wn_off);
+      ++g;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();  // every wave is done with the last step's slot
+    __builtin_amdgcn_sched_barrier(0);
+    float* stage = reinterpret_cast<float*>(s_tiles + ((g + S - 1) % S) * ST) + wave * kStageFloats;
+    store_wave_tile<MI, NI>(acc, out, p.out_f32, p.n, r0, rlim, c0, p.n, stage);
+  }
+  if constexpr (MODE != kTransTN) zero_outside_window(p, win);
 }
 
 KArgs make_args(const GemmProblem& p) {
@@ -701,20 +897,24 @@ int pick_forward_tile(const GemmProblem& p) {
   return p.n >= 256 ? kT128x256 : kT128x128;
 }
 
-// trans_ragged_dot: the contraction runs over a group's rows, often short, so
-// two co-resident workgroups per CU (128 x 128, 2 stages) hide each other's
-// pipeline fill and epilogue better than one deep pipeline.
+// trans_ragged_dot: the contraction runs over a group's rows.  Short groups
+// (at most 256 rows on average) make the kernel a stream of dW writes, where
+// 256 x 256 tiles cut the per-tile overhead; longer groups do best with two
+// co-resident workgroups per CU (128 x 128, 2 stages) hiding each other's
+// pipeline fill and epilogue.
 int pick_trans_tile(const GemmProblem& p) {
   const int forced = forced_tile("RD_TRANS_TILE");
   if (forced >= 0) return forced;
-  (void)p;
-  return kT128x128x2;
+  const long long avg_rows = p.m / (p.num_local > 0 ? p.num_local : 1);
+  return avg_rows <= 256 && p.k >= 256 && p.n >= 256 ? kT256x256 : kT128x128x2;
 }
 
-template <int MODE, int BM, int BN, int S>
+template <int MODE, int BM, int BN, int S, int KS = 32, int WGS = 1>
 void launch_one(const KArgs& a, long long work, hipStream_t stream) {
-  grouped_gemm_kernel<MODE, BM, BN, S><<<grid_size(work, (S > 0 && S != 2) || BM * BN > 128 * 128 ? 1 : 2),
-                                        kThreads, 0, stream>>>(a);
+  if constexpr (S == 0)
+    grouped_gemm_regs<MODE, BM, BN><<<grid_size(work, 2), kThreads, 0, stream>>>(a);
+  else
+    grouped_gemm_stream<MODE, BM, BN, S, KS, WGS><<<grid_size(work, WGS), kThreads, 0, stream>>>(a);
 }
 
 template <int MODE>
@@ -726,11 +926,14 @@ void launch_tile(int tile, const KArgs& a, const GemmProblem& p, hipStream_t str
            (p.m + kZeroRows - 1) / kZeroRows + 2;
   };
   switch (tile) {
-    case kT64x128: launch_one<MODE, 64, 128, 6>(a, work(64, 128), stream); break;
-    case kT128x256: launch_one<MODE, 128, 256, 3>(a, work(128, 256), stream); break;
-    case kT256x256: launch_one<MODE, 256, 256, 2>(a, work(256, 256), stream); break;
-    case kT128x128x2: launch_one<MODE, 128, 128, 2>(a, work(128, 128), stream); break;
-    default: launch_one<MODE, 128, 128, 4>(a, work(128, 128), stream); break;
+    // 64-deep stages (measured faster than 32-deep ones with more stages: the
+    // per-stage barrier costs more than the extra depth gains); the LDS ring
+    // takes 128-144 KB, 64 KB per workgroup for the two-per-CU variant
+    case kT64x128: launch_one<MODE, 64, 128, 6, 64>(a, work(64, 128), stream); break;
+    case kT128x256: launch_one<MODE, 128, 256, 3, 64>(a, work(128, 256), stream); break;
+    case kT256x256: launch_one<MODE, 256, 256, 2, 64>(a, work(256, 256), stream); break;
+    case kT128x128x2: launch_one<MODE, 128, 128, 2, 64, 2>(a, work(128, 128), stream); break;
+    default: launch_one<MODE, 128, 128, 4, 64>(a, work(128, 128), stream); break;
   }
 }
 
