@@ -537,11 +537,14 @@ struct FwdTiles {
 
 // trans_ragged_dot tiles: every local group owns ka x nc output tiles of
 // dW[j]; the contraction runs over the group's rows.  Groups are visited
-// largest first (s_order); each XCD owns a contiguous slice of the n-tiles,
-// so it streams only its slice of dy while every XCD reads the narrower x.
+// largest first (s_order).  The eight XCDs form an xa x xc grid: XCD
+// (xa_i, xc_i) owns the a-tiles of slice xa_i and the c-tiles of slice xc_i of
+// every group, so each XCD does an equal share of every group and a row block
+// of x (dy) is fetched by xc (xa) XCDs.  The grid shape minimises that
+// re-read traffic, k * xc + n * xa.
 struct TransTiles {
   long long per_x, slots;
-  int ka, nc, ncx;
+  int ka, nc, kax, ncx, xc;
   bool split;
   struct Tile {
     int j, r_begin, r_end, a0, c0, nk;
@@ -549,9 +552,24 @@ struct TransTiles {
   __device__ __forceinline__ void init(int gl, int k, int n, int BM, int BN) {
     ka = (k + BM - 1) / BM;
     nc = (n + BN - 1) / BN;
-    split = nc >= kXcds;
-    ncx = split ? (nc + kXcds - 1) / kXcds : nc;
-    per_x = static_cast<long long>(gl) * ka * ncx;
+    int xa = 0;
+    xc = 0;
+    long long best = 0;
+    for (int a = 1; a <= kXcds; a *= 2) {
+      const int c = kXcds / a;
+      if (a > ka || c > nc) continue;
+      const long long cost = static_cast<long long>(k) * c + static_cast<long long>(n) * a;
+      if (xa == 0 || cost < best) {
+        xa = a;
+        xc = c;
+        best = cost;
+      }
+    }
+    split = xa > 0;
+    if (!split) xa = xc = 1;
+    kax = (ka + xa - 1) / xa;
+    ncx = (nc + xc - 1) / xc;
+    per_x = static_cast<long long>(gl) * kax * ncx;
     slots = split ? per_x * kXcds : per_x;
   }
   template <int BM, int BN, int KS = BK>
@@ -562,11 +580,11 @@ struct TransTiles {
       x = static_cast<int>(s % kXcds);
       i = s / kXcds;
     }
-    const int q = static_cast<int>(i / (static_cast<long long>(ka) * ncx));
-    const int rem = static_cast<int>(i - static_cast<long long>(q) * ka * ncx);
-    const int at = rem / ncx;
-    const int ct = x * ncx + (rem - at * ncx);
-    if (ct >= nc) return false;
+    const int q = static_cast<int>(i / (static_cast<long long>(kax) * ncx));
+    const int rem = static_cast<int>(i - static_cast<long long>(q) * kax * ncx);
+    const int at = (x / xc) * kax + rem / ncx;
+    const int ct = (x % xc) * ncx + rem % ncx;
+    if (at >= ka || ct >= nc) return false;
     t.j = s_order[q];
     t.r_begin = s_lb[t.j];
     t.r_end = s_lb[t.j + 1];
@@ -873,9 +891,9 @@ int grid_size(long long work_items, int per_cu) {
 // Tile shapes (BM x BN, LDS stages) of the buffer-to-LDS pipeline.  Every
 // shape runs 4 waves in a 2 x 2 layout; larger wave tiles read fewer LDS bytes
 // per MFMA, smaller BM wastes fewer MFMA rows on short groups.
-enum Tile { kT64x128 = 0, kT128x128 = 1, kT128x256 = 2, kT256x256 = 3, kT128x128x2 = 4, kTileCount };
+enum Tile { kT64x128 = 0, kT128x128 = 1, kT128x256 = 2, kT256x256 = 3, kT128x128x2 = 4, kT64x64 = 5, kTileCount };
 
-// RD_FWD_TILE / RD_TRANS_TILE (0..4) force a shape, for tile sweeps.
+// RD_FWD_TILE / RD_TRANS_TILE (0..5) force a shape, for tile sweeps.
 int forced_tile(const char* name) {
   const char* v = getenv(name);
   if (v == nullptr || *v == 0) return -1;
@@ -885,7 +903,7 @@ int forced_tile(const char* name) {
 
 // Forward shape from what the host knows (never the device-resident group
 // sizes): m / num_local bounds the mean rows per local group.  Decode-sized
-// groups take the 64-row tile; otherwise a 128 x 256 tile when n allows it
+// groups take a 64-row tile; otherwise a 128 x 256 tile when n allows it
 // (fewer passes over each row block of x), else 128 x 128.  Chosen from a
 // sweep of every shape on the up-projection, backward, window+limit and
 // decode workloads.
@@ -893,7 +911,7 @@ int pick_forward_tile(const GemmProblem& p) {
   const int forced = forced_tile("RD_FWD_TILE");
   if (forced >= 0) return forced;
   const long long avg_rows = p.m / (p.num_local > 0 ? p.num_local : 1);
-  if (avg_rows <= 48) return kT64x128;
+  if (avg_rows <= 48) return kT64x128;  // decode: weight streaming (64 x 64 measured slower)
   return p.n >= 256 ? kT128x256 : kT128x128;
 }
 
@@ -933,6 +951,7 @@ void launch_tile(int tile, const KArgs& a, const GemmProblem& p, hipStream_t str
     case kT128x256: launch_one<MODE, 128, 256, 3, 64>(a, work(128, 256), stream); break;
     case kT256x256: launch_one<MODE, 256, 256, 2, 64>(a, work(256, 256), stream); break;
     case kT128x128x2: launch_one<MODE, 128, 128, 2, 64, 2>(a, work(128, 128), stream); break;
+    case kT64x64: launch_one<MODE, 64, 64, 8, 64>(a, work(64, 64), stream); break;
     default: launch_one<MODE, 128, 128, 4, 64>(a, work(128, 128), stream); break;
   }
 }
