@@ -30,7 +30,8 @@ int check_dims(int64_t m, int64_t k, int64_t n) {
 
 int forward_common(const void* x, const void* w, const int32_t* group_sizes, int32_t num_groups,
                    const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* out,
-                   int32_t out_dtype, int64_t m, int64_t k, int64_t n, void* stream, bool trans_rhs) {
+                   int32_t out_dtype, int64_t m, int64_t k, int64_t n, void* workspace, size_t workspace_bytes,
+                   void* stream, bool trans_rhs) {
   int st = check_dims(m, k, n);
   if (st != RD_OK) return st;
   st = check_groups(num_groups, group_offset, num_local);
@@ -39,7 +40,7 @@ int forward_common(const void* x, const void* w, const int32_t* group_sizes, int
   if (!w || !group_sizes) return RD_EINVAL;
   if (m == 0) return RD_OK;  // no rows: x and out may be empty (null)
   if (!x || !out) return RD_EINVAL;
-  if (!aligned16(x) || !aligned16(w) || !aligned16(out)) return RD_EINVAL;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(out) || !aligned16(workspace)) return RD_EINVAL;
   if ((reinterpret_cast<uintptr_t>(group_sizes) & 3u) || (reinterpret_cast<uintptr_t>(limit) & 3u))
     return RD_EINVAL;
   rd::GemmProblem p{};
@@ -55,7 +56,18 @@ int forward_common(const void* x, const void* w, const int32_t* group_sizes, int
   p.m = static_cast<int>(m);
   p.k = static_cast<int>(k);
   p.n = static_cast<int>(n);
-  return rd::launch_forward(p, trans_rhs, static_cast<hipStream_t>(stream));
+  return rd::launch_forward(p, trans_rhs, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+// The GemmProblem of a forward call of these sizes (pointers unset).
+rd::GemmProblem shape_only(int64_t m, int64_t k, int64_t n, int32_t num_local) {
+  rd::GemmProblem p{};
+  p.num_groups = num_local;
+  p.num_local = num_local;
+  p.m = static_cast<int>(m);
+  p.k = static_cast<int>(k);
+  p.n = static_cast<int>(n);
+  return p;
 }
 
 }  // namespace
@@ -74,19 +86,26 @@ const char* rd_status_string(int status) {
   }
 }
 
+size_t rd_forward_workspace_size(int64_t m, int64_t k, int64_t n, int32_t num_local, int32_t trans_rhs) {
+  if (check_dims(m, k, n) != RD_OK || num_local < 1 || num_local > RD_MAX_GROUPS) return 0;
+  const rd::DecodePlan d = rd::plan_decode(shape_only(m, k, n, num_local), trans_rhs != 0);
+  return d.use ? d.ws_bytes : 0;
+}
+
 int rd_forward(const void* x, const void* w, const int32_t* group_sizes, int32_t num_groups,
                const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* out,
-               int32_t out_dtype, int64_t m, int64_t k, int64_t n, void* stream) {
+               int32_t out_dtype, int64_t m, int64_t k, int64_t n, void* workspace, size_t workspace_bytes,
+               void* stream) {
   return forward_common(x, w, group_sizes, num_groups, group_offset, num_local, limit, out, out_dtype, m,
-                        k, n, stream, false);
+                        k, n, workspace, workspace_bytes, stream, false);
 }
 
 int rd_forward_trans_rhs(const void* x, const void* w, const int32_t* group_sizes,
                          int32_t num_groups, const int32_t* group_offset, int32_t num_local,
                          const int32_t* limit, void* out, int32_t out_dtype, int64_t m, int64_t k,
-                         int64_t n, void* stream) {
+                         int64_t n, void* workspace, size_t workspace_bytes, void* stream) {
   return forward_common(x, w, group_sizes, num_groups, group_offset, num_local, limit, out, out_dtype, m,
-                        k, n, stream, true);
+                        k, n, workspace, workspace_bytes, stream, true);
 }
 
 size_t rd_trans_workspace_size(int64_t m, int64_t k, int64_t n, int32_t num_local) {

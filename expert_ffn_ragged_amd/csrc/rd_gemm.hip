@@ -864,6 +864,229 @@ __global__ __launch_bounds__(kThreads, WGS) void grouped_gemm_stream(KArgs p) {
   if constexpr (MODE != kTransTN) zero_outside_window(p, win);
 }
 
+// ---------------------------------------------------------------- decode: split contraction
+
+// ragged_dot with a few rows per group (decode: ~5 rows per expert) is a
+// stream of expert weights; its speed is set by how evenly the weight bytes
+// are spread over the CUs and by how little else interrupts the stream.
+// Work is counted in steps: a block is (32-row block of a group, NW columns)
+// and has k / 16 steps of 16 contraction rows.  The grid splits the
+// concatenated step list into equal contiguous ranges, one per workgroup
+// (so every CU streams the same number of weight bytes), and a range crosses
+// block boundaries wherever they fall.  A workgroup keeps the fp32 sums of
+// the blocks its range touches in registers (two at a time) and writes them,
+// for the block's valid rows only, when its range is done: a store in flight
+// would otherwise hold the next load wait (the counter does not tell loads
+// from stores).  decode_streamk_reduce adds the partial sums of each block
+// in workgroup order (deterministic: a bf16 result is the RNE of the f32 one)
+// and applies the window and limit rules.  Per step, wave w loads 16 x 16 B
+// of the row block (lanes 0..15) and NB KB of the weight slab; the slab is
+// stored as it sits in memory (MNLayout) and fed to the MFMA through the LDS
+// transpose read.
+constexpr int kDecKS = 16;  // contraction rows per step: one MFMA k-slice
+constexpr int kDecBM = 32;  // rows per block: one MFMA row block
+
+// The step split shared by both decode kernels.
+struct StepSplit {
+  int nnc, spb;   // column strips, steps per block
+  long long per;  // steps per workgroup
+  __device__ __forceinline__ void init(int total_m, int n, int nw, int k, int grid) {
+    nnc = n / nw;
+    spb = k / kDecKS;
+    const long long total = static_cast<long long>(total_m) * nnc * spb;
+    per = (total + grid - 1) / grid;
+    if (per < 1) per = 1;
+  }
+};
+
+template <int NB, int S>
+__global__ __launch_bounds__(kThreads, 1) void decode_streamk_gemm(KArgs p, float* __restrict__ ws, int seg_max) {
+  constexpr int NW = 128 * NB;                   // block columns: 4 waves x NB MFMA blocks of 32
+  constexpr int A_BYTES = kDecBM * kDecKS * 2;   // 1 KB
+  constexpr int B_BYTES = kDecKS * NW * 2;
+  constexpr int ST = A_BYTES + B_BYTES;          // bytes per ring slot
+  constexpr int BI = B_BYTES / 4096;             // 1 KB weight loads per wave per step (= NB)
+  constexpr int L = BI + 1;                      // loads per wave per step
+  static_assert(BI * 4096 == B_BYTES, "weight step must split into 1 KB slices per wave");
+  __shared__ __attribute__((aligned(1024))) char s_ring[S * ST];
+  __shared__ int s_lb[RD_MAX_GROUPS + 1];
+  __shared__ int s_aux[RD_MAX_GROUPS + 1];
+  __shared__ long long s_wave[kThreads / 64];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  build_local_bounds(p.gs, p.G, p.offp, p.gl, p.limp, p.m, s_lb, s_wave);
+  const int total_m = tile_prefix(s_lb, p.gl, kDecBM, s_aux, s_wave);
+  StepSplit sp;
+  sp.init(total_m, p.n, NW, p.k, gridDim.x);
+  const long long total = static_cast<long long>(total_m) * sp.nnc * sp.spb;
+  const long long s_begin = static_cast<long long>(blockIdx.x) * sp.per;
+  const long long s_end = min(s_begin + sp.per, total);
+  if (s_begin >= s_end) return;  // uniform: this workgroup has no steps
+  const long long first_blk = s_begin / sp.spb;
+
+  struct Block {
+    int j, row0, nrows, n0;
+  };
+  auto block_at = [&](long long i, Block& d) {
+    const int mt = static_cast<int>(i / sp.nnc);
+    d.n0 = static_cast<int>(i % sp.nnc) * NW;
+    d.j = upper_index(s_aux, p.gl, mt);
+    d.row0 = s_lb[d.j] + (mt - s_aux[d.j]) * kDecBM;
+    d.nrows = min(kDecBM, s_lb[d.j + 1] - d.row0);
+  };
+
+  const uint32_t ring = lds_address(s_ring);
+  const int nsteps = static_cast<int>(s_end - s_begin);
+  const int kt0 = static_cast<int>(s_begin - first_blk * sp.spb);  // step of the first block to start at
+  // producer: steps issued, current block and step in it, the block's buffer
+  // resources and per-lane offsets (no divisions per step)
+  int issued = 0, p_kt = kt0;
+  long long p_blk = first_blk;
+  bool p_new = true;
+  u32x4_t ra, rb;
+  uint32_t va = 0, vb[BI];
+  auto produce = [&]() {
+    if (issued >= nsteps) return;
+    if (p_kt == sp.spb) {
+      ++p_blk;
+      p_kt = 0;
+      p_new = true;
+    }
+    if (p_new) {
+      Block d;
+      block_at(p_blk, d);
+      // rows past the block's valid rows read as zeros (buffer range check)
+      ra = uniform(make_rsrc(p.a + static_cast<long long>(d.row0) * p.k,
+                             static_cast<unsigned long long>(d.nrows) * p.k * 2));
+      rb = uniform(make_rsrc(p.b + static_cast<long long>(d.j) * p.k * p.n,
+                             static_cast<unsigned long long>(p.k) * p.n * 2));
+      const int c = wave * 16 + (lane & 15);  // row-block chunk: row c / 2, 16-byte half c % 2
+      va = static_cast<uint32_t>(c >> 1) * p.k * 2 + (c & 1) * 16;
+#pragma unroll
+      for (int q = 0; q < BI; ++q) {
+        const int cq = (wave * BI + q) * 64 + lane;
+        const int row = cq / (NW / 8), slot = cq % (NW / 8);
+        vb[q] = static_cast<uint32_t>(row) * p.n * 2 + (d.n0 + ((slot ^ MNLayout<NW>::swz(row)) << 3)) * 2;
+      }
+      p_new = false;
+    }
+    const uint32_t slot = ring + (issued % S) * ST;
+    const int kr = p_kt * kDecKS;
+    if (lane < 16) dma16(ra, slot + wave * 256, va, uniform(static_cast<uint32_t>(kr) * 2));
+    const uint32_t sb = uniform(static_cast<uint32_t>(kr) * p.n * 2);
+#pragma unroll
+    for (int q = 0; q < BI; ++q) dma16(rb, slot + A_BYTES + (wave * BI + q) * 1024, vb[q], sb);
+    ++p_kt;
+    ++issued;
+  };
+
+  // Partial sums of block segment seg, valid rows only: lane l holds column
+  // l % 32 of rows 8 * (v / 4) + 4 * (l / 32) + v % 4.
+  auto store_partials = [&](const f32x16_t (&v)[NB], long long blk, long long seg) {
+    if (seg >= seg_max) return;  // cannot happen: seg_max bounds the blocks one range touches
+    Block d;
+    block_at(blk, d);
+    float* dst = ws + ((static_cast<long long>(blockIdx.x) * seg_max + seg) * kDecBM) * NW + wave * NB * 32 +
+                 (lane & 31);
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+      if (8 * jb >= d.nrows) break;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 8 * jb + 4 * (lane >> 5) + i;
+        if (r < d.nrows) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) dst[r * NW + nb * 32] = v[nb][4 * jb + i];
+        }
+      }
+    }
+  };
+
+#pragma unroll
+  for (int i = 0; i < S - 1; ++i) produce();
+
+  f32x16_t acc[NB], prev[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16_t{};
+  long long prev_blk = -1, c_blk = first_blk;
+  int c_kt = kt0;
+  for (int g = 0; g < nsteps; ++g) {
+    __builtin_amdgcn_sched_barrier(0);
+    wait_ladder<L, S - 2>(issued - 1 - g);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    produce();
+    const char* slot = s_ring + (g % S) * ST;
+    const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(slot + (((lane & 31) << 1) + (lane >> 5)) * 16);
+    const uint16_t* tb = reinterpret_cast<const uint16_t*>(slot + A_BYTES);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const bf16x8_t bf = MNOperand<NW>::frag(tb, (wave * NB + nb) * 32, 0);
+      acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc[nb], 0, 0, 0);
+    }
+    if (++c_kt == sp.spb && g + 1 < nsteps) {  // a block ends inside the range
+      if (prev_blk >= 0) store_partials(prev, prev_blk, prev_blk - first_blk);  // a third block: rare
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        prev[nb] = acc[nb];
+        acc[nb] = f32x16_t{};
+      }
+      prev_blk = c_blk;
+      ++c_blk;
+      c_kt = 0;
+    }
+  }
+  if (prev_blk >= 0) store_partials(prev, prev_blk, prev_blk - first_blk);
+  store_partials(acc, c_blk, c_blk - first_blk);
+}
+
+// out[r, :] = sum of the partial sums of r's block, in workgroup order, for
+// rows of the window; +0 for the other rows below L; rows >= L untouched.
+template <int NB>
+__global__ __launch_bounds__(kThreads) void decode_streamk_reduce(KArgs p, const float* __restrict__ ws, int seg_max,
+                                                                  int grid) {
+  constexpr int NW = 128 * NB;
+  __shared__ int s_lb[RD_MAX_GROUPS + 1];
+  __shared__ int s_aux[RD_MAX_GROUPS + 1];
+  __shared__ long long s_wave[kThreads / 64];
+  const Window win = build_local_bounds(p.gs, p.G, p.offp, p.gl, p.limp, p.m, s_lb, s_wave);
+  const int total_m = tile_prefix(s_lb, p.gl, kDecBM, s_aux, s_wave);
+  StepSplit sp;
+  sp.init(total_m, p.n, NW, p.k, grid);
+  const int cpr = p.n / 8;
+  const long long total = static_cast<long long>(win.L) * cpr;
+  for (long long e = static_cast<long long>(blockIdx.x) * kThreads + threadIdx.x; e < total;
+       e += static_cast<long long>(gridDim.x) * kThreads) {
+    const int r = static_cast<int>(e / cpr);
+    const int c = static_cast<int>(e - static_cast<long long>(r) * cpr) * 8;
+    f32x4_t lo = f32x4_t{0.f, 0.f, 0.f, 0.f}, hi = lo;
+    if (r >= win.lo && r < win.hi) {
+      const int j = upper_index(s_lb, p.gl, r);
+      const int mt = s_aux[j] + (r - s_lb[j]) / kDecBM, rr = (r - s_lb[j]) % kDecBM;
+      const int nc = c / NW;
+      const long long i = static_cast<long long>(mt) * sp.nnc + nc;
+      const long long b0 = i * sp.spb / sp.per, b1 = ((i + 1) * sp.spb - 1) / sp.per;
+      for (long long b = b0; b <= b1; ++b) {
+        const long long seg = i - b * sp.per / sp.spb;
+        if (b >= grid || seg >= seg_max) break;  // cannot happen (see decode_streamk_gemm)
+        const float* src = ws + ((b * seg_max + seg) * kDecBM + rr) * NW + (c - nc * NW);
+        lo += *reinterpret_cast<const f32x4_t*>(src);
+        hi += *reinterpret_cast<const f32x4_t*>(src + 4);
+      }
+    }
+    const long long o = static_cast<long long>(r) * p.n + c;
+    if (p.out_f32) {
+      *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.out) + o) = lo;
+      *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.out) + o + 4) = hi;
+    } else {
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + o) =
+          make_uint4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
+                     pack_bf16x2(hi[2], hi[3]));
+    }
+  }
+}
+
 KArgs make_args(const GemmProblem& p) {
   KArgs a{};
   a.a = static_cast<const uint16_t*>(p.a);
@@ -960,10 +1183,61 @@ void launch_tile(int tile, const KArgs& a, const GemmProblem& p, hipStream_t str
 // offsets, so each operand must span less than 4 GiB.
 bool fits_32bit(long long a, long long b) { return a * b * 2 < (1ll << 32); }
 
+// Split-contraction decode path (decode_streamk_gemm): chosen from host-known
+// sizes when groups average at most 24 rows, n splits into 768-, 512- or
+// 256-column strips and k into 16-row steps.  One workgroup per CU; the
+// workspace holds seg_max partial blocks per workgroup, seg_max bounding the
+// blocks one range can touch (from at most ceil(m/32) + num_local row blocks);
+// it must fit in 256 MiB.  RD_DECODE=0 turns the path off (for sweeps).
+DecodePlan plan_decode_impl(const GemmProblem& p, bool trans_rhs) {
+  DecodePlan d{};
+  const char* env = getenv("RD_DECODE");
+  if (trans_rhs || (env != nullptr && env[0] == '0')) return d;
+  const long long avg_rows = p.m / (p.num_local > 0 ? p.num_local : 1);
+  if (p.m <= 0 || avg_rows > 24 || p.k % kDecKS != 0 || !fits_32bit(p.m, p.k) || !fits_32bit(p.k, p.n)) return d;
+  const int nb = p.n % 768 == 0 ? 6 : p.n % 512 == 0 ? 4 : p.n % 256 == 0 ? 2 : 0;
+  if (nb == 0) return d;
+  const long long grid = device_cu_count();
+  const long long nnc = p.n / (128 * nb), spb = p.k / kDecKS;
+  const long long blocks_max = ((p.m + kDecBM - 1) / kDecBM + p.num_local) * nnc;
+  const long long per_max = (blocks_max * spb + grid - 1) / grid;
+  const long long seg_max = (per_max + spb - 1) / spb + 1;
+  const unsigned long long ws =
+      static_cast<unsigned long long>(grid) * seg_max * kDecBM * (128ull * nb) * sizeof(float);
+  if (ws > (256ull << 20)) return d;
+  d.use = true;
+  d.nb = nb;
+  d.grid = static_cast<int>(grid);
+  d.seg_max = static_cast<int>(seg_max);
+  d.ws_bytes = ws;
+  return d;
+}
+
+template <int NB, int S>
+void launch_decode(const KArgs& a, const GemmProblem& p, const DecodePlan& d, float* ws, hipStream_t stream) {
+  decode_streamk_gemm<NB, S><<<d.grid, kThreads, 0, stream>>>(a, ws, d.seg_max);
+  const long long chunks = (static_cast<long long>(p.m) * (p.n / 8) + kThreads - 1) / kThreads;
+  decode_streamk_reduce<NB><<<grid_size(chunks, 4), kThreads, 0, stream>>>(a, ws, d.seg_max, d.grid);
+}
+
 }  // namespace
 
-int launch_forward(const GemmProblem& p, bool trans_rhs, hipStream_t stream) {
+DecodePlan plan_decode(const GemmProblem& p, bool trans_rhs) { return plan_decode_impl(p, trans_rhs); }
+
+int launch_forward(const GemmProblem& p, bool trans_rhs, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
   const KArgs a = make_args(p);
+  const DecodePlan d = plan_decode_impl(p, trans_rhs);
+  if (d.use && workspace != nullptr && workspace_bytes >= d.ws_bytes) {
+    float* ws = static_cast<float*>(workspace);
+    switch (d.nb) {
+      // ring: 6 x 25 KB, 8 x 17 KB, 8 x 9 KB
+      case 6: launch_decode<6, 6>(a, p, d, ws, stream); break;
+      case 4: launch_decode<4, 8>(a, p, d, ws, stream); break;
+      default: launch_decode<2, 8>(a, p, d, ws, stream); break;
+    }
+    return hipGetLastError() == hipSuccess ? RD_OK : RD_EHIP;
+  }
   const bool dma = (p.k % BK) == 0 && fits_32bit(p.m, p.k) && fits_32bit(p.k, p.n);
   if (dma) {
     const int tile = pick_forward_tile(p);

@@ -22,7 +22,18 @@ struct GemmProblem {
   int m, k, n;
 };
 
-int launch_forward(const GemmProblem& p, bool trans_rhs, hipStream_t stream);
+// Workspace plan of the split-contraction decode path (use == false: the
+// forward needs no workspace).
+struct DecodePlan {
+  bool use;
+  int nb, grid, seg_max;
+  size_t ws_bytes;
+};
+DecodePlan plan_decode(const GemmProblem& p, bool trans_rhs);
+
+// workspace may be null; the decode path runs only with ws_bytes of it.
+int launch_forward(const GemmProblem& p, bool trans_rhs, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
 int launch_trans(const GemmProblem& p, hipStream_t stream);
 int launch_glu_fwd(const void* fused, const int32_t* limit, void* out, int rows, int h, hipStream_t stream);
 int launch_glu_bwd(const void* fused, const void* d_out, const int32_t* limit, void* d_fused, int rows, int h,

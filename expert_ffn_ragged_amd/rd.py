@@ -18,6 +18,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librd.so")
 
+ABI_VERSION = 2
 RD_OK, RD_EINVAL, RD_EUNSUPPORTED, RD_EHIP = 0, 1, 2, 3
 RD_BF16, RD_F32 = 0, 1
 _DTYPES = {torch.bfloat16: RD_BF16, torch.float32: RD_F32}
@@ -25,6 +26,7 @@ _DTYPES = {torch.bfloat16: RD_BF16, torch.float32: RD_F32}
 EXPORTS = (
     "rd_abi_version",
     "rd_status_string",
+    "rd_forward_workspace_size",
     "rd_forward",
     "rd_forward_trans_rhs",
     "rd_trans_workspace_size",
@@ -54,7 +56,9 @@ def library():
     lib.rd_abi_version.argtypes = []
     lib.rd_status_string.restype = ctypes.c_char_p
     lib.rd_status_string.argtypes = [ctypes.c_int]
-    fwd = [vp, vp, vp, i32, vp, i32, vp, vp, i32, i64, i64, i64, vp]
+    lib.rd_forward_workspace_size.restype = sz
+    lib.rd_forward_workspace_size.argtypes = [i64, i64, i64, i32, i32]
+    fwd = [vp, vp, vp, i32, vp, i32, vp, vp, i32, i64, i64, i64, vp, sz, vp]
     for name in ("rd_forward", "rd_forward_trans_rhs"):
         getattr(lib, name).restype = ctypes.c_int
         getattr(lib, name).argtypes = fwd
@@ -66,7 +70,7 @@ def library():
     lib.rd_glu_fwd.argtypes = [vp, vp, vp, i64, i64, vp]
     lib.rd_glu_bwd.restype = ctypes.c_int
     lib.rd_glu_bwd.argtypes = [vp, vp, vp, vp, i64, i64, vp]
-    if lib.rd_abi_version() != 1:
+    if lib.rd_abi_version() != ABI_VERSION:
         raise RDError("librd.so ABI version mismatch")
     _lib = lib
     return lib
@@ -110,14 +114,16 @@ def _scalar(t, name):
 
 
 def ragged_dot(x, w, group_sizes, group_offset=None, limit=None, trans_rhs=False,
-               out_dtype=torch.bfloat16, out=None, stream=None):
+               out_dtype=torch.bfloat16, out=None, workspace=None, stream=None):
     """out[rows of local group j] = x[rows] @ w[j] (or @ w[j].T with trans_rhs).
 
     x: [m, k] bf16; w: [num_local, k, n] bf16 ([num_local, n, k] with trans_rhs);
     group_sizes: [G] int32 on the GPU; group_offset, limit: optional (1,) int32
     GPU tensors.  Rows below the limit outside the local window are +0; rows
     at or past the limit are left as they were in ``out`` (uninitialised when
-    ``out`` is not given).
+    ``out`` is not given).  ``workspace``: optional uint8 GPU scratch; when the
+    sizes call for one (decode shapes) and none of sufficient size is given,
+    one is allocated.
     """
     _need(x, "x", torch.bfloat16, 2)
     _need(w, "w", torch.bfloat16, 3)
@@ -137,9 +143,14 @@ def ragged_dot(x, w, group_sizes, group_offset=None, limit=None, trans_rhs=False
     _need(out, "out", out.dtype, 2)
     if tuple(out.shape) != (m, n) or out.dtype not in _DTYPES:
         raise ValueError("out must be [m, n] bf16 or float32")
-    fn = library().rd_forward_trans_rhs if trans_rhs else library().rd_forward
+    lib = library()
+    ws_bytes = lib.rd_forward_workspace_size(m, k, n, gl, 1 if trans_rhs else 0)
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    fn = lib.rd_forward_trans_rhs if trans_rhs else lib.rd_forward
     _check(fn(_ptr(x), _ptr(w), _ptr(group_sizes), group_sizes.numel(), _ptr(group_offset), gl,
-              _ptr(limit), _ptr(out), _DTYPES[out.dtype], m, k, n, _stream(stream)))
+              _ptr(limit), _ptr(out), _DTYPES[out.dtype], m, k, n,
+              _ptr(workspace) if ws_bytes else None, ws_bytes, _stream(stream)))
     return out
 
 

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define RD_ABI_VERSION 1
+#define RD_ABI_VERSION 2
 
 /* status codes */
 #define RD_OK 0
@@ -72,6 +72,19 @@ int rd_abi_version(void);
 const char* rd_status_string(int status);
 
 /*
+ * Workspace (device scratch, caller-owned) that rd_forward (trans_rhs == 0)
+ * or rd_forward_trans_rhs (trans_rhs != 0) can use for these sizes: 0 when
+ * the call needs none.  Currently nonzero only for decode-sized forward calls
+ * (at most 24 rows per local group on average, k a multiple of 16, n a
+ * multiple of 256), where every CU streams an equal share of the weight
+ * bytes and the fp32 partial sums of blocks shared by two CUs are added in a
+ * second, fixed-order pass.  The size (at most 256 MiB) grows with
+ * (m / 32 + num_local) and depends on the current device's CU count.
+ * Returns 0 for sizes the entry points would reject.
+ */
+size_t rd_forward_workspace_size(int64_t m, int64_t k, int64_t n, int32_t num_local, int32_t trans_rhs);
+
+/*
  * ragged_dot ([SkyRL]; window from fast_ragged_dot; limit from [MaxText]).
  *
  *   x            [m, k] bf16: rows sorted by group.
@@ -90,23 +103,32 @@ const char* rd_status_string(int status);
  * other row below L is written as +0.  Rows >= L are neither read (in x)
  * nor written (in out).
  *
+ * workspace/workspace_bytes: NULL/0, or device scratch of at least
+ * rd_forward_workspace_size(m, k, n, num_local, 0) bytes, 16-byte aligned,
+ * not shared with a concurrently running call.  With less than that size the
+ * call runs without the split-contraction path (same results within the
+ * GEMM tolerance, slower for decode shapes).  Its contents on entry do not
+ * matter and are undefined on return.
+ *
  * Requirements: m >= 0; k, n > 0 and multiples of 8; 1 <= num_local <=
  * num_groups <= RD_MAX_GROUPS; m, k, n < 2^31.  With m == 0 nothing is
  * launched and x, out may be NULL.
  */
 int rd_forward(const void* x, const void* w, const int32_t* group_sizes, int32_t num_groups,
                const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* out,
-               int32_t out_dtype, int64_t m, int64_t k, int64_t n, void* stream);
+               int32_t out_dtype, int64_t m, int64_t k, int64_t n, void* workspace, size_t workspace_bytes,
+               void* stream);
 
 /*
  * ragged_dot with trans_rhs ([SkyRL], the dx rule of the backward):
  * identical to rd_forward except that w is [num_local, n, k] and
  * out[r,:] = x[r,:] @ w[j]^T, i.e. the contraction runs over w's last dim.
+ * Its workspace size is rd_forward_workspace_size(m, k, n, num_local, 1).
  */
 int rd_forward_trans_rhs(const void* x, const void* w, const int32_t* group_sizes,
                          int32_t num_groups, const int32_t* group_offset, int32_t num_local,
                          const int32_t* limit, void* out, int32_t out_dtype, int64_t m, int64_t k,
-                         int64_t n, void* stream);
+                         int64_t n, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * trans_ragged_dot ([SkyRL], _gpu_trans_ragged_dot_fwd; the weight

@@ -46,7 +46,7 @@ def test_links_the_same_hip_runtime_soname_as_torch():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.rd_abi_version() == 1
+    assert lib.rd_abi_version() == rd.ABI_VERSION == 2
     for s in (0, 1, 2, 3, 99):
         assert isinstance(lib.rd_status_string(s), bytes)
     assert lib.rd_trans_workspace_size(100, 64, 64, 4) == 0
@@ -57,7 +57,7 @@ def _fwd(lib, **kw):
     a.update(kw)
     v = lambda p: None if p is None else ctypes.c_void_p(p)
     return lib.rd_forward(v(a["x"]), v(a["w"]), v(a["gs"]), a["G"], v(a["off"]), a["gl"], v(a["limit"]),
-                          v(a["out"]), a["dt"], a["m"], a["k"], a["n"], None)
+                          v(a["out"]), a["dt"], a["m"], a["k"], a["n"], v(a.get("ws")), a.get("ws_bytes", 0), None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -75,6 +75,7 @@ def _fwd(lib, **kw):
     (dict(G=2000, gl=2000), rd.RD_EUNSUPPORTED),
     (dict(G=0, gl=0), rd.RD_EINVAL),
     (dict(m=1 << 31), rd.RD_EUNSUPPORTED),
+    (dict(ws=40, ws_bytes=64), rd.RD_EINVAL),  # misaligned workspace
     (dict(m=0), rd.RD_OK),                 # nothing to do, nothing launched
 ])
 def test_forward_rejects_bad_arguments_before_launch(lib, kw, status):
@@ -95,3 +96,15 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(rd, "LIB_PATH", "/nonexistent/librd.so")
     with pytest.raises(rd.RDError):
         rd.library()
+
+
+def test_forward_workspace_size_follows_the_decode_rule(lib):
+    """Only decode-sized forward calls (<= 24 rows per local group on average) ask for a workspace."""
+    ws = lib.rd_forward_workspace_size(512, 4096, 1536, 128, 0)
+    assert 0 < ws <= 256 << 20 and ws % 16 == 0
+    assert lib.rd_forward_workspace_size(512, 4096, 1536, 128, 1) == 0      # trans_rhs: none
+    assert lib.rd_forward_workspace_size(8192, 4096, 2048, 64, 0) == 0      # prefill-sized groups
+    assert lib.rd_forward_workspace_size(512, 4104, 1536, 128, 0) == 0      # k not a multiple of 16
+    assert lib.rd_forward_workspace_size(512, 4096, 136, 128, 0) == 0       # n: no 256-column strips
+    assert lib.rd_forward_workspace_size(512, 12, 1536, 128, 0) == 0        # invalid k
+    assert lib.rd_forward_workspace_size(512, 4096, 1536, 0, 0) == 0        # invalid num_local

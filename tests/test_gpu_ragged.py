@@ -177,6 +177,63 @@ def test_empty_rows_is_a_no_op():
     assert bool((dw == 0).all())
 
 
+# ------------------------------------------------------------ decode shapes (split-contraction path)
+
+def _decode_sizes(G, seed, empty_frac=0.3, big=None):
+    """Mostly 0..8 rows per group, ~30% empty, optionally one group longer than a 32-row block."""
+    rng = np.random.default_rng(seed)
+    gs = rng.integers(1, 9, size=G).astype(np.int32)
+    gs[rng.permutation(G)[:int(empty_frac * G)]] = 0
+    if big is not None:
+        gs[big] = 45
+    return gs
+
+
+@pytest.mark.parametrize("n", [256, 512, 768, 1536])
+@pytest.mark.parametrize("mode", ["plain", "limit", "window"])
+def test_decode_split_path(n, mode):
+    G, k = 24, 512
+    gs_host = _decode_sizes(G, 60 + n, big=5)
+    m = int(gs_host.sum()) + 7
+    off, gl, limit = None, G, None
+    if mode == "window":
+        off, gl = 8, 12
+    if mode == "limit":
+        limit = int(gs_host.sum()) - 30
+    assert m // gl <= 24
+    lib = rd.library()
+    assert lib.rd_forward_workspace_size(m, k, n, gl, 0) > 0, "decode sizes must take the split path"
+    say(f"decode split path n={n} mode={mode} m={m} G={G} gl={gl}")
+    x, w, gs = _case(m, k, n, gs_host, gl, 90 + n, nan_from=limit)
+    o32, o16 = run_forward(x, w, gs, off=off, limit=limit)
+    check_forward_full(x, w, gs_host, off, limit, False, o32, o16, f"decode n={n} {mode}")
+
+
+def test_decode_split_matches_unsplit_path_and_repeats_bitwise():
+    """Without a workspace the same call runs the tile path; both agree within the GEMM tolerance."""
+    G, k, n = 32, 1024, 768
+    gs_host = _decode_sizes(G, 71)
+    m = int(gs_host.sum())
+    x, w, gs = _case(m, k, n, gs_host, G, 72)
+    lib = rd.library()
+    ws_bytes = lib.rd_forward_workspace_size(m, k, n, G, 0)
+    assert ws_bytes > 0
+    say(f"decode split vs unsplit m={m} k={k} n={n}")
+    a = rd.ragged_dot(x, w, gs, out_dtype=torch.float32)
+    b = rd.ragged_dot(x, w, gs, out_dtype=torch.float32)
+    c = sentinel((m, n), torch.float32)
+    import ctypes
+    st = lib.rd_forward(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.data_ptr()), ctypes.c_void_p(gs.data_ptr()),
+                        G, None, G, None, ctypes.c_void_p(c.data_ptr()), rd.RD_F32, m, k, n, None, 0,
+                        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == rd.RD_OK
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    ref = oracle.ragged_dot(bits(x), bits(w), gs_host)
+    assert_gemm_close(a.cpu().numpy(), ref, "split")
+    assert_gemm_close(c.cpu().numpy(), ref, "unsplit")
+
+
 def test_repeat_runs_are_bitwise_identical():
     say("determinism")
     gs_host = workloads.random_sizes(16, 3000, seed=8, empty=(3,))
