@@ -442,27 +442,45 @@ constexpr int kStageFloats = 16 * kStagePitch;  // per wave
 // l holds column l % 32 of rows 8*(v/4) + 4*(l/32) + v%4; half h takes v/4 in
 // {2h, 2h+1}), so 32 lanes fill 128 contiguous bytes of a row per write;
 // then every lane reads 8 consecutive floats of one row, rounds them (bf16,
-// round-to-nearest-even) or keeps them (f32), and issues 16-byte stores.  No
-// accumulator is copied into general registers wholesale, which keeps
-// 256-accumulator tiles unspilled.  LDS operations of one wave run in order,
-// so the area is reused safely.
-template <int MI, int NI>
+// round-to-nearest-even) or keeps them (f32), and issues 16-byte stores.  The
+// NI blocks of one row half are staged side by side (NI areas of
+// kStageFloats) before any is read back, so the LDS write-to-read latency is
+// paid once per NI blocks.  No accumulator is copied into general registers
+// wholesale, which keeps 256-accumulator tiles unspilled.  LDS operations of
+// one wave run in order, so the areas are reused safely.
+// Largest divisor of NI whose staging areas (4 waves x NB x kStageFloats
+// floats) fit in `elems` bf16 elements of LDS.
+constexpr int epilogue_batch(int NI, int elems) {
+  int best = 0;
+  for (int nb = 1; nb <= NI; ++nb)
+    if (NI % nb == 0 && 4 * nb * kStageFloats * 2 <= elems) best = nb;
+  return best;
+}
+
+template <int MI, int NI, int NB = NI>
 __device__ __forceinline__ void store_wave_tile(const f32x16_t (&acc)[MI][NI], void* out, bool f32, long long ld,
                                                 int r0, int rlim, int c0, int clim, float* stage) {
+  static_assert(NI % NB == 0, "blocks staged together must divide NI");
   const int l = threadIdx.x & 63;
   const int rr = l >> 2, cc = (l & 3) * 8;  // read-back: row rr of the half, columns cc .. cc+7
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int n0 = 0; n0 < NI; n0 += NB) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int v = 8 * h; v < 8 * h + 8; ++v)
-          stage[(8 * (v >> 2) - 16 * h + 4 * (l >> 5) + (v & 3)) * kStagePitch + (l & 31)] = acc[mi][ni][v];
-        const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(stage + rr * kStagePitch + cc);
-        const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(stage + rr * kStagePitch + cc + 4);
-        const int grow = r0 + mi * 32 + 16 * h + rr, gcol = c0 + ni * 32 + cc;
+          stage[b * kStageFloats + (8 * (v >> 2) - 16 * h + 4 * (l >> 5) + (v & 3)) * kStagePitch + (l & 31)] =
+              acc[mi][n0 + b][v];
+      const int grow = r0 + mi * 32 + 16 * h + rr;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(stage + b * kStageFloats + rr * kStagePitch + cc);
+        const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(stage + b * kStageFloats + rr * kStagePitch + cc + 4);
+        const int gcol = c0 + (n0 + b) * 32 + cc;
         if (grow < rlim && gcol < clim) {
           if (f32) {
             float* o = static_cast<float*>(out) + grow * ld + gcol;
@@ -474,8 +492,9 @@ __device__ __forceinline__ void store_wave_tile(const f32x16_t (&acc)[MI][NI], v
             *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + grow * ld + gcol) = v;
           }
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 // Zeros for a wave's block (a local group with no rows gets an all +0 dW).
@@ -648,14 +667,14 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_regs(KArgs p) {
   constexpr int MI = WM / 32, NI = WN / 32;
   constexpr int A_EL = BM * BK, B_EL = BN * BK;
   __shared__ __attribute__((aligned(1024))) uint16_t s_tiles[2 * (A_EL + B_EL)];
-  static_assert(4 * kStageFloats * 2 <= 2 * (A_EL + B_EL), "epilogue staging must fit");
+  static_assert(4 * NI * kStageFloats * 2 <= 2 * (A_EL + B_EL), "epilogue staging must fit");
   __shared__ int s_lb[RD_MAX_GROUPS + 1];
   __shared__ int s_aux[RD_MAX_GROUPS + 1];
   __shared__ long long s_wave[kThreads / 64];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm_off = (wave >> 1) * WM, wn_off = (wave & 1) * WN;
-  float* stage = reinterpret_cast<float*>(s_tiles) + wave * kStageFloats;
+  float* stage = reinterpret_cast<float*>(s_tiles) + wave * NI * kStageFloats;
   const Window win = build_local_bounds(p.gs, p.G, p.offp, p.gl, p.limp, p.m, s_lb, s_wave);
 
   if constexpr (MODE == kFwdNN || MODE == kFwdNT) {
@@ -755,7 +774,8 @@ __global__ __launch_bounds__(kThreads, WGS) void grouped_gemm_stream(KArgs p) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int MI = WM / 32, NI = WN / 32;
   constexpr int A_EL = BM * KS, B_EL = BN * KS, ST = A_EL + B_EL;
-  static_assert(4 * kStageFloats * 2 <= ST, "epilogue staging must fit in one ring slot");
+  constexpr int EPI = epilogue_batch(NI, ST);
+  static_assert(EPI >= 1 && 4 * EPI * kStageFloats * 2 <= ST, "epilogue staging must fit in one ring slot");
   using Ops = StreamOps<MODE, BM, BN, KS>;
   using OpA = typename Ops::A;
   using OpB = typename Ops::B;
@@ -858,8 +878,8 @@ __global__ __launch_bounds__(kThreads, WGS) void grouped_gemm_stream(KArgs p) {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();  // every wave is done with the last step's slot
     __builtin_amdgcn_sched_barrier(0);
-    float* stage = reinterpret_cast<float*>(s_tiles + ((g + S - 1) % S) * ST) + wave * kStageFloats;
-    store_wave_tile<MI, NI>(acc, out, p.out_f32, p.n, r0, rlim, c0, p.n, stage);
+    float* stage = reinterpret_cast<float*>(s_tiles + ((g + S - 1) % S) * ST) + wave * EPI * kStageFloats;
+    store_wave_tile<MI, NI, EPI>(acc, out, p.out_f32, p.n, r0, rlim, c0, p.n, stage);
   }
   if constexpr (MODE != kTransTN) zero_outside_window(p, win);
 }
@@ -1114,9 +1134,10 @@ int grid_size(long long work_items, int per_cu) {
 // Tile shapes (BM x BN, LDS stages) of the buffer-to-LDS pipeline.  Every
 // shape runs 4 waves in a 2 x 2 layout; larger wave tiles read fewer LDS bytes
 // per MFMA, smaller BM wastes fewer MFMA rows on short groups.
-enum Tile { kT64x128 = 0, kT128x128 = 1, kT128x256 = 2, kT256x256 = 3, kT128x128x2 = 4, kT64x64 = 5, kTileCount };
+enum Tile { kT64x128 = 0, kT128x128 = 1, kT128x256 = 2, kT256x256 = 3, kT128x128x2 = 4, kT64x64 = 5, kT256x256k32 = 6,
+            kT128x256k32 = 7, kT128x256x2 = 8, kT128x128k32x2 = 9, kTileCount };
 
-// RD_FWD_TILE / RD_TRANS_TILE (0..5) force a shape, for tile sweeps.
+// RD_FWD_TILE / RD_TRANS_TILE (0..9) force a shape, for tile sweeps.
 int forced_tile(const char* name) {
   const char* v = getenv(name);
   if (v == nullptr || *v == 0) return -1;
@@ -1126,28 +1147,31 @@ int forced_tile(const char* name) {
 
 // Forward shape from what the host knows (never the device-resident group
 // sizes): m / num_local bounds the mean rows per local group.  Decode-sized
-// groups take a 64-row tile; otherwise a 128 x 256 tile when n allows it
-// (fewer passes over each row block of x), else 128 x 128.  Chosen from a
-// sweep of every shape on the up-projection, backward, window+limit and
-// decode workloads.
-int pick_forward_tile(const GemmProblem& p) {
+// groups take a 64-row tile (when no workspace allows the split-contraction
+// path); groups of up to 256 rows on average take 128 x 256 tiles with two
+// workgroups per CU (one multiplies while the other drains its stores);
+// longer groups take 128 x 256 with one workgroup and a 3-stage ring, as does
+// every trans_rhs call.  Chosen from sweeps of every shape on the
+// up-projection, backward, window+limit and decode workloads.
+int pick_forward_tile(const GemmProblem& p, bool trans_rhs) {
   const int forced = forced_tile("RD_FWD_TILE");
   if (forced >= 0) return forced;
   const long long avg_rows = p.m / (p.num_local > 0 ? p.num_local : 1);
-  if (avg_rows <= 48) return kT64x128;  // decode: weight streaming (64 x 64 measured slower)
-  return p.n >= 256 ? kT128x256 : kT128x128;
+  if (avg_rows <= 48) return kT64x128;
+  if (p.n < 256) return kT128x128;
+  return !trans_rhs && avg_rows <= 256 ? kT128x256x2 : kT128x256;
 }
 
 // trans_ragged_dot: the contraction runs over a group's rows.  Short groups
-// (at most 256 rows on average) make the kernel a stream of dW writes, where
-// 256 x 256 tiles cut the per-tile overhead; longer groups do best with two
-// co-resident workgroups per CU (128 x 128, 2 stages) hiding each other's
-// pipeline fill and epilogue.
+// (at most 256 rows on average) make the kernel a stream of dW writes; two
+// co-resident 128 x 256 workgroups per CU overlap one's stores with the
+// other's multiplies.  Longer groups do best with two 128 x 128 workgroups
+// per CU and 64-deep stages.
 int pick_trans_tile(const GemmProblem& p) {
   const int forced = forced_tile("RD_TRANS_TILE");
   if (forced >= 0) return forced;
   const long long avg_rows = p.m / (p.num_local > 0 ? p.num_local : 1);
-  return avg_rows <= 256 && p.k >= 256 && p.n >= 256 ? kT256x256 : kT128x128x2;
+  return avg_rows <= 256 && p.k >= 128 && p.n >= 256 ? kT128x256x2 : kT128x128x2;
 }
 
 template <int MODE, int BM, int BN, int S, int KS = 32, int WGS = 1>
@@ -1175,6 +1199,10 @@ void launch_tile(int tile, const KArgs& a, const GemmProblem& p, hipStream_t str
     case kT256x256: launch_one<MODE, 256, 256, 2, 64>(a, work(256, 256), stream); break;
     case kT128x128x2: launch_one<MODE, 128, 128, 2, 64, 2>(a, work(128, 128), stream); break;
     case kT64x64: launch_one<MODE, 64, 64, 8, 64>(a, work(64, 64), stream); break;
+    case kT256x256k32: launch_one<MODE, 256, 256, 4, 32>(a, work(256, 256), stream); break;
+    case kT128x256k32: launch_one<MODE, 128, 256, 6, 32>(a, work(128, 256), stream); break;
+    case kT128x256x2: launch_one<MODE, 128, 256, 2, 32, 2>(a, work(128, 256), stream); break;
+    case kT128x128k32x2: launch_one<MODE, 128, 128, 3, 32, 2>(a, work(128, 128), stream); break;
     default: launch_one<MODE, 128, 128, 4, 64>(a, work(128, 128), stream); break;
   }
 }
@@ -1240,7 +1268,7 @@ int launch_forward(const GemmProblem& p, bool trans_rhs, void* workspace, size_t
   }
   const bool dma = (p.k % BK) == 0 && fits_32bit(p.m, p.k) && fits_32bit(p.k, p.n);
   if (dma) {
-    const int tile = pick_forward_tile(p);
+    const int tile = pick_forward_tile(p, trans_rhs);
     if (trans_rhs)
       launch_tile<kFwdNT>(tile, a, p, stream);
     else

@@ -1,0 +1,204 @@
+"""Summaries of rocprofv3 output for the ragged-dot kernels, and their lookup.
+
+Turns the CSV files of ``rocprofv3 --kernel-trace --stats`` and of
+``rocprofv3 --pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` / MFMA-counter runs of
+``bench.py`` into short Markdown summaries (kept under ``profiles/``), and
+reads the HBM traffic back for ``bench.py``'s roofline.
+
+HBM bytes: ``FETCH_SIZE`` and ``WRITE_SIZE`` (KiB per dispatch, summed over
+the L2 channels) are scaled by what the same counter reads for a plain copy
+kernel of known size (``bench.py --copy-calib`` copies 256 MiB), so that the
+reported bytes are calibrated against an operation whose traffic is known.
+A summary records a digest of the kernel sources; ``bench.py`` reports the
+traffic only while the digest still matches (the kernels have not changed
+since the counters were taken).
+
+Usage (on the host, after copying the rocprofv3 output directories back)::
+
+    python -m expert_ffn_ragged_amd.profiling traffic --fetch DIR --write DIR \\
+        [--mfma DIR] --command "..." --out profiles/upproj_fwd_bwd_traffic.md
+    python -m expert_ffn_ragged_amd.profiling stats --stats DIR --command "..." --out FILE.md
+"""
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CALIB_BYTES = 256 << 20  # the calibration copy of bench.py --copy-calib
+SIMDS = 1024             # 256 CUs x 4 SIMDs
+XCDS = 8
+
+# bench.py op name <- kernel name pattern (one kernel per op in the step)
+OP_OF_KERNEL = (
+    (r"grouped_gemm_stream<0,", "ragged_dot"),
+    (r"grouped_gemm_stream<1,", "ragged_dot_trans_rhs"),
+    (r"grouped_gemm_stream<2,", "trans_ragged_dot"),
+    (r"glu_fwd_kernel", "glu_fwd"),
+    (r"glu_bwd_kernel", "glu_bwd"),
+    (r"decode_streamk_gemm", "decode_gemm"),
+    (r"decode_streamk_reduce", "decode_reduce"),
+)
+
+
+def source_digest():
+    """sha256 (16 hex digits) of the kernel sources and the C header."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(HERE, "csrc", "*"))) + [os.path.join(ROOT, "include", "rd.h")]
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(kernel):
+    k = kernel.replace("void ", "").replace("rd::(anonymous namespace)::", "")
+    k = re.sub(r"\(rd::KArgs\)|\(KArgs.*", "", k)
+    return re.sub(r"\(.*", "", k).strip()
+
+
+def op_of(kernel):
+    for pat, op in OP_OF_KERNEL:
+        if re.search(pat, kernel):
+            return op
+    return None
+
+
+def _rows(directory, suffix):
+    for f in sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)):
+        with open(f) as fh:
+            yield from csv.DictReader(fh)
+
+
+def counter_means(directory):
+    """{(kernel short name, counter): (mean value, dispatches)} over a counter_collection CSV."""
+    acc = {}
+    calib = {}
+    for row in _rows(directory, "counter_collection.csv"):
+        name, ctr, val = row["Kernel_Name"], row["Counter_Name"], float(row["Counter_Value"])
+        if "copyBuffer" in name:
+            calib.setdefault(ctr, []).append((int(row["Grid_Size"]), val))
+            continue
+        if op_of(name) is None:
+            continue
+        acc.setdefault((short_name(name), ctr), []).append(val)
+    means = {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+    # the calibration copy is the largest copyBuffer dispatch
+    cal = {}
+    for ctr, vals in calib.items():
+        big = max(g for g, _ in vals)
+        sel = [v for g, v in vals if g == big]
+        cal[ctr] = sum(sel) / len(sel)
+    return means, cal
+
+
+def traffic_summary(fetch_dir, write_dir, mfma_dir, command):
+    fm, fcal = counter_means(fetch_dir)
+    wm, wcal = counter_means(write_dir)
+    fscale = CALIB_BYTES / (fcal["FETCH_SIZE"] * 1024)
+    wscale = CALIB_BYTES / (wcal["WRITE_SIZE"] * 1024)
+    lines = [
+        "# HBM traffic per launch: MoE up-projection fwd+bwd step (m8192 k4096 n2048 g64 Zipf 1.1), MI355X",
+        "",
+        "Commands (from the repository root on the GPU box, `cd /tmp && export TMPDIR=/tmp` first; one",
+        "counter per run, each run its own process):",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        f"Calibration: a 256 MiB device-to-device copy (`__amd_rocclr_copyBuffer`) reads FETCH_SIZE = "
+        f"{fcal['FETCH_SIZE']:.0f} KiB and WRITE_SIZE = {wcal['WRITE_SIZE']:.0f} KiB, so bytes = "
+        f"FETCH_SIZE x 1024 x {fscale:.4f} and WRITE_SIZE x 1024 x {wscale:.4f}.",
+        "",
+        f"source digest: {source_digest()}",
+        "",
+        "| op | kernel | dispatches | read (bytes) | write (bytes) | traffic (bytes) |",
+        "|---|---|---|---|---|---|",
+    ]
+    for (name, ctr), (val, n) in sorted(fm.items()):
+        if ctr != "FETCH_SIZE":
+            continue
+        w = wm.get((name, "WRITE_SIZE"), (0.0, 0))[0]
+        rb, wb = val * 1024 * fscale, w * 1024 * wscale
+        lines.append(f"| {op_of(name)} | `{name}` | {n} | {rb:.4g} | {wb:.4g} | {rb + wb:.4g} |")
+    if mfma_dir:
+        mm, _ = counter_means(mfma_dir)
+        lines += ["", "MFMA counters (same command with `--pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 "
+                  "GRBM_GUI_ACTIVE SQ_BUSY_CYCLES`). MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+                  f"(GRBM_GUI_ACTIVE / {XCDS} x {SIMDS} SIMDs); MFMA flop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512.",
+                  "", "| op | kernel | MFMA busy | MFMA flop per launch |", "|---|---|---|---|"]
+        names = sorted({n for n, c in mm if c == "SQ_VALU_MFMA_BUSY_CYCLES"})
+        for name in names:
+            busy = mm[(name, "SQ_VALU_MFMA_BUSY_CYCLES")][0]
+            gui = mm[(name, "GRBM_GUI_ACTIVE")][0]
+            mops = mm.get((name, "SQ_INSTS_VALU_MFMA_MOPS_BF16"), (0.0, 0))[0]
+            util = busy / (gui / XCDS * SIMDS) if gui else 0.0
+            lines.append(f"| {op_of(name)} | `{name}` | {util:.3f} | {mops * 512:.4g} |")
+    return "\n".join(lines) + "\n"
+
+
+def stats_summary(stats_dir, command, title):
+    rows = []
+    for row in _rows(stats_dir, "kernel_stats.csv"):
+        if op_of(row["Name"]) is None:
+            continue
+        rows.append((short_name(row["Name"]), int(row["Calls"]), float(row["AverageNs"]) / 1e3,
+                     float(row["MinNs"]) / 1e3, float(row["MaxNs"]) / 1e3))
+    lines = [f"# Kernel durations: {title}", "", "Command (from the repository root on the GPU box, "
+             "`cd /tmp && export TMPDIR=/tmp` first):", "", "```", command, "```", "",
+             f"source digest: {source_digest()}", "",
+             "| kernel | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
+    for name, calls, avg, mn, mx in sorted(rows, key=lambda r: -r[2]):
+        lines.append(f"| `{name}` | {calls} | {avg:.1f} | {mn:.1f} | {mx:.1f} |")
+    return "\n".join(lines) + "\n"
+
+
+def load_traffic(path):
+    """{op: traffic bytes per launch} from a traffic summary whose digest matches the sources, else {}."""
+    if not os.path.exists(path):
+        return {}
+    text = open(path).read()
+    m = re.search(r"^source digest: (\w+)", text, flags=re.M)
+    if not m or m.group(1) != source_digest():
+        return {}
+    out = {}
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) == 6 and cells[0] not in ("op", "---"):
+            try:
+                out[cells[0]] = float(cells[5])
+            except ValueError:
+                pass
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description="summaries of rocprofv3 output for the ragged-dot kernels")
+    sub = ap.add_subparsers(dest="what", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--mfma")
+    t.add_argument("--command", required=True)
+    t.add_argument("--out", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("--stats", required=True)
+    s.add_argument("--command", required=True)
+    s.add_argument("--title", required=True)
+    s.add_argument("--out", required=True)
+    a = ap.parse_args()
+    text = (traffic_summary(a.fetch, a.write, a.mfma, a.command) if a.what == "traffic"
+            else stats_summary(a.stats, a.command, a.title))
+    with open(a.out, "w") as fh:
+        fh.write(text)
+    print(text)
+
+
+if __name__ == "__main__":
+    main()
