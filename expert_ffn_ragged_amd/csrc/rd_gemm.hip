@@ -248,6 +248,7 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 // there (the slot map is an involution).
 template <int ROWS, int KS>
 struct KDma {
+  static constexpr int kFragReads = 1;  // LDS reads per MFMA fragment
   static constexpr int kCh = KS / 8;
   static constexpr int kRowsPerSlice = 64 / kCh;
   static constexpr int kInstr = ROWS / kRowsPerSlice / 4;  // 1 KB slices per wave per stage
@@ -284,6 +285,7 @@ struct KDma {
 // slot ^ swz(row).
 template <int COLS, int KS>
 struct MNDma {
+  static constexpr int kFragReads = 2;  // LDS reads per MFMA fragment (two transposed 64-bit reads)
   static constexpr int kCpr = COLS / 8;
   static constexpr int kRowsPerSlice = 512 / COLS;
   static constexpr int kInstr = KS * COLS / 2048;
@@ -314,32 +316,48 @@ struct MNDma {
   }
 };
 
-// MFMAs of one KS-deep stage.  Fragments are double-buffered across its
-// 16-deep slices: slice ks+1 is read from LDS while slice ks multiplies, and a
-// scheduling fence per slice keeps at most two fragment sets live (with 256
-// accumulators per lane a deeper hoist would spill).
+// MFMAs of one KS-deep stage, in 16-deep slices with double-buffered
+// fragments: stage_frags loads slice 0 (called right after the stage's
+// barrier, before the next stage's loads are issued, so their issue covers the
+// LDS latency); mma_stage then, for each slice, first issues the LDS reads of
+// the next slice and then the slice's MFMAs (a scheduling group pins that
+// order, so every read has a whole slice of MFMAs to land).  A fence per slice
+// keeps at most two fragment sets live (with 256 accumulators per lane a
+// deeper hoist would spill).
+template <class OpA, class OpB, int MI, int NI>
+struct StageFrags {
+  bf16x8_t a[2][MI], b[2][NI];
+};
+
+template <class OpA, class OpB, int MI, int NI>
+__device__ __forceinline__ void stage_frags(const uint16_t* ta, const uint16_t* tb, StageFrags<OpA, OpB, MI, NI>& f,
+                                            int wm_off, int wn_off) {
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) f.a[0][mi] = OpA::frag(ta, wm_off + mi * 32, 0);
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) f.b[0][ni] = OpB::frag(tb, wn_off + ni * 32, 0);
+}
+
 template <class OpA, class OpB, int MI, int NI, int KS = BK>
-__device__ __forceinline__ void mma_stage(const uint16_t* ta, const uint16_t* tb, f32x16_t (&acc)[MI][NI],
-                                          int wm_off, int wn_off) {
-  bf16x8_t af[2][MI], bfr[2][NI];
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi) af[0][mi] = OpA::frag(ta, wm_off + mi * 32, 0);
-#pragma unroll
-  for (int ni = 0; ni < NI; ++ni) bfr[0][ni] = OpB::frag(tb, wn_off + ni * 32, 0);
+__device__ __forceinline__ void mma_stage(const uint16_t* ta, const uint16_t* tb, StageFrags<OpA, OpB, MI, NI>& f,
+                                          f32x16_t (&acc)[MI][NI], int wm_off, int wn_off) {
+  constexpr int kReads = MI * OpA::kFragReads + NI * OpB::kFragReads;
 #pragma unroll
   for (int ks = 0; ks < KS / 16; ++ks) {
     const int cur = ks & 1;
     if (ks + 1 < KS / 16) {
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) af[cur ^ 1][mi] = OpA::frag(ta, wm_off + mi * 32, ks + 1);
+      for (int mi = 0; mi < MI; ++mi) f.a[cur ^ 1][mi] = OpA::frag(ta, wm_off + mi * 32, ks + 1);
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) bfr[cur ^ 1][ni] = OpB::frag(tb, wn_off + ni * 32, ks + 1);
+      for (int ni = 0; ni < NI; ++ni) f.b[cur ^ 1][ni] = OpB::frag(tb, wn_off + ni * 32, ks + 1);
     }
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][mi], bfr[cur][ni], acc[mi][ni], 0, 0, 0);
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[cur][mi], f.b[cur][ni], acc[mi][ni], 0, 0, 0);
+    if (ks + 1 < KS / 16) __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);  // next slice's LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, MI * NI, 0);                       // then this slice's MFMAs
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -870,9 +888,13 @@ __global__ __launch_bounds__(kThreads, WGS) void grouped_gemm_stream(KArgs p) {
       wait_ladder<L, S - 2>(issued - 1 - g);
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      produce();
       const uint16_t* slot = s_tiles + (g % S) * ST;
-      mma_stage<OpA, OpB, MI, NI, KS>(slot, slot + A_EL, acc, wm_off, wn_off);
+      StageFrags<OpA, OpB, MI, NI> fr;
+      stage_frags(slot, slot + A_EL, fr, wm_off, wn_off);
+      __builtin_amdgcn_sched_barrier(0);
+      produce();
+      __builtin_amdgcn_sched_barrier(0);
+      mma_stage<OpA, OpB, MI, NI, KS>(slot, slot + A_EL, fr, acc, wm_off, wn_off);
       ++g;
     }
     __builtin_amdgcn_sched_barrier(0);
