@@ -15,6 +15,8 @@ from oracle.bf16 import bf16_bits_to_f32, bf16_bits_to_f64, f32_to_bf16_bits
 
 from tests import test_oracle_glu as pg
 from tests import test_oracle_ragged as pr
+from tests import test_oracle_unsort as pu
+import oracle.unsort as ouns
 
 
 def _fails(fn, *args):
@@ -210,3 +212,57 @@ def test_missing_negative_zero_map_is_caught(monkeypatch):
 
     monkeypatch.setattr(oracle, "glu_bwd", mutant)
     assert _caught(_glu_pins())
+
+
+# ---------------------------------------------------------------- unsort_bwd_rows mutants
+
+
+def _unsort_pins():
+    for args in ((1, 1.0, 1.0), (4, 1e-38, 0.5)):
+        yield pu.test_grad_matches_exact_two_step_rounding, args
+    yield pu.test_float32_intermediate_decides_double_rounding_cases, ()
+    yield pu.test_special_weights, ()
+    yield pu.test_dot_is_exact_sum_of_products, ()
+    yield pu.test_dot_special_rows, ()
+    for args in ((4, 4), (-5, 0), (100, 9)):
+        yield pu.test_limit_clamps_and_drops_rows, args
+
+
+def _unsort_with(grad_fn=None, dot_fn=None, limit_fn=None):
+    def mutant(g, y, w, limit=None):
+        g = np.asarray(g, dtype=np.uint16)
+        y = np.asarray(y, dtype=np.uint16)
+        w = np.asarray(w, dtype=np.float32)
+        rows = g.shape[0]
+        L = limit_fn(limit, rows) if limit_fn else (rows if limit is None else min(max(int(limit), 0), rows))
+        gd = grad_fn(g[:L], w[:L]) if grad_fn else f32_to_bf16_bits(bf16_bits_to_f32(g[:L]) * w[:L, None])
+        dt = dot_fn(g[:L], y[:L]) if dot_fn else (bf16_bits_to_f64(g[:L]) * bf16_bits_to_f64(y[:L])).sum(axis=1)
+        return gd, dt
+    return mutant
+
+
+def _one_rounding(g, w):
+    """the product rounded once from its exact value (float64) instead of through float32"""
+    p = bf16_bits_to_f64(g) * w.astype(np.float64)[:, None]
+    b = p.view(np.uint64)
+    keep = (b >> 45) & 1
+    r = (b + ((1 << 44) - 1) + keep) >> 45          # RNE to 8 significand bits, then back to float32 layout
+    f = ((r << 45).view(np.float64)).astype(np.float32)
+    return f32_to_bf16_bits(f)
+
+
+def _shifted_weight(g, w):
+    return f32_to_bf16_bits(bf16_bits_to_f32(g) * np.roll(w, 1)[:, None])
+
+
+@pytest.mark.parametrize("mutant", [
+    _unsort_with(grad_fn=_one_rounding),
+    _unsort_with(grad_fn=_shifted_weight),
+    _unsort_with(dot_fn=lambda g, y: (bf16_bits_to_f64(g) * bf16_bits_to_f64(g)).sum(axis=1)),
+    _unsort_with(dot_fn=lambda g, y: (bf16_bits_to_f64(g) * bf16_bits_to_f64(y))[:, 1:].sum(axis=1)),
+    _unsort_with(limit_fn=lambda limit, rows: rows),
+    _unsort_with(limit_fn=lambda limit, rows: rows if limit is None else min(max(int(limit), 0) + 1, rows)),
+], ids=["one-rounding", "shifted-weight", "dot-g-squared", "dot-drops-column", "limit-ignored", "limit-off-by-one"])
+def test_unsort_mutants_are_caught(monkeypatch, mutant):
+    monkeypatch.setattr(ouns, "unsort_bwd_rows", mutant)
+    assert _caught(_unsort_pins())
