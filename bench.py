@@ -210,6 +210,19 @@ def extra_all(steps):
     for key, nbytes in (("glu_fwd", L * h * 6), ("glu_bwd", L * h * 10)):
         out[f"window_limit_{key}"] = {"ms": round(per[key], 4), "GB/s": round(nbytes / per[key] / 1e6, 1),
                                       "hbm_frac": round(nbytes / per[key] / 1e6 / HBM_PEAK_GBS, 4)}
+    del d, o, g, gb
+    torch.cuda.empty_cache()
+    # weighted unsort backward over the packed buffer's valid rows
+    d = workloads.make(4, "cuda", parts=("ug", "uy", "uw"))
+    hid = d["k"]
+    grad = torch.empty((d["m"], hid), dtype=torch.bfloat16, device="cuda")
+    dot = torch.empty((d["m"],), dtype=torch.float32, device="cuda")
+    _, _, per = timed_ops([("unsort", lambda: rd.unsort_bwd_rows(d["ug"], d["uy"], d["uw"], lim, grad=grad, dot=dot))],
+                          steps, 3)
+    nbytes = L * (3 * hid * 2 + 8)  # g, y read, grad written (bf16); w read, dot written (f32)
+    out["window_limit_unsort_bwd_rows"] = {"ms": round(per["unsort"], 4), "GB/s": round(nbytes / per["unsort"] / 1e6, 1),
+                                           "hbm_frac": round(nbytes / per["unsort"] / 1e6 / HBM_PEAK_GBS, 4),
+                                           "algorithmic_bytes": int(nbytes)}
     return out
 
 

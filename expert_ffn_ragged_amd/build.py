@@ -28,6 +28,7 @@ COMMON = [
 SOURCES = [
     ("rd_gemm.hip", []),
     ("rd_glu.hip", ["-ffp-contract=off"]),
+    ("rd_unsort.hip", []),
     ("rd_api.cpp", ["-x", "hip"]),
 ]
 

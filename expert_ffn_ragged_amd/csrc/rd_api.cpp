@@ -80,7 +80,7 @@ const char* rd_status_string(int status) {
   switch (status) {
     case RD_OK: return "ok";
     case RD_EINVAL: return "invalid argument (null or misaligned pointer, bad size or dtype)";
-    case RD_EUNSUPPORTED: return "unsupported size (k, n, h must be multiples of 8; dims < 2^31; groups <= RD_MAX_GROUPS)";
+    case RD_EUNSUPPORTED: return "unsupported size (k, n, h, hidden must be multiples of 8; dims < 2^31; groups <= RD_MAX_GROUPS)";
     case RD_EHIP: return "HIP runtime error while launching";
     default: return "unknown status";
   }
@@ -172,6 +172,20 @@ int rd_glu_bwd(const void* fused, const void* d_out, const int32_t* limit, void*
     return RD_EINVAL;
   return rd::launch_glu_bwd(fused, d_out, limit, d_fused, static_cast<int>(rows), static_cast<int>(h),
                             static_cast<hipStream_t>(stream));
+}
+
+int rd_unsort_bwd_rows(const void* g, const void* y, const float* w, const int32_t* limit, void* grad, float* dot,
+                       int64_t rows, int64_t hidden, void* stream) {
+  if (rows < 0 || hidden <= 0) return RD_EINVAL;
+  if ((hidden % 8) != 0) return RD_EUNSUPPORTED;
+  if (rows >= (int64_t(1) << 31) || hidden >= (int64_t(1) << 30)) return RD_EUNSUPPORTED;
+  if (rows == 0) return RD_OK;  // no rows: the buffers may be empty (null)
+  if (!g || !y || !w || !grad || !dot) return RD_EINVAL;
+  if (!aligned16(g) || !aligned16(y) || !aligned16(grad) || (reinterpret_cast<uintptr_t>(w) & 3u) ||
+      (reinterpret_cast<uintptr_t>(dot) & 3u) || (reinterpret_cast<uintptr_t>(limit) & 3u))
+    return RD_EINVAL;
+  return rd::launch_unsort_bwd_rows(g, y, w, limit, grad, dot, static_cast<int>(rows), static_cast<int>(hidden),
+                                    static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

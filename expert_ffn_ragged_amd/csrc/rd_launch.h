@@ -39,6 +39,9 @@ int launch_glu_fwd(const void* fused, const int32_t* limit, void* out, int rows,
 int launch_glu_bwd(const void* fused, const void* d_out, const int32_t* limit, void* d_fused, int rows, int h,
                    hipStream_t stream);
 
+int launch_unsort_bwd_rows(const void* g, const void* y, const float* w, const int32_t* limit, void* grad,
+                           float* dot, int rows, int hidden, hipStream_t stream);
+
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 

@@ -33,6 +33,7 @@ EXPORTS = (
     "rd_trans",
     "rd_glu_fwd",
     "rd_glu_bwd",
+    "rd_unsort_bwd_rows",
 )
 
 
@@ -70,6 +71,8 @@ def library():
     lib.rd_glu_fwd.argtypes = [vp, vp, vp, i64, i64, vp]
     lib.rd_glu_bwd.restype = ctypes.c_int
     lib.rd_glu_bwd.argtypes = [vp, vp, vp, vp, i64, i64, vp]
+    lib.rd_unsort_bwd_rows.restype = ctypes.c_int
+    lib.rd_unsort_bwd_rows.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, vp]
     if lib.rd_abi_version() != ABI_VERSION:
         raise RDError("librd.so ABI version mismatch")
     _lib = lib
@@ -215,3 +218,29 @@ def glu_bwd(fused, d_out, limit=None, out=None, stream=None):
         raise ValueError("out must be [rows, 2h]")
     _check(library().rd_glu_bwd(_ptr(fused), _ptr(d_out), _ptr(limit), _ptr(out), rows, h, _stream(stream)))
     return out
+
+
+def unsort_bwd_rows(g, y, w, limit=None, grad=None, dot=None, stream=None):
+    """(grad, dot) over rows r < limit: grad = bf16(f32(g) * w[r]), dot[r] = sum_c g[r, c] * y[r, c] (float32).
+
+    g, y: [rows, hidden] bf16 in the packed buffer's row order; w: [rows] float32 routing weights.
+    Rows at or past the limit are left as they were in ``grad`` and ``dot`` (uninitialised when not given).
+    """
+    _need(g, "g", torch.bfloat16, 2)
+    _need(y, "y", torch.bfloat16, 2)
+    _need(w, "w", torch.float32, 1)
+    limit = _scalar(limit, "limit")
+    rows, hidden = g.shape
+    if tuple(y.shape) != (rows, hidden) or w.shape[0] != rows:
+        raise ValueError("g and y must be [rows, hidden] and w [rows]")
+    if grad is None:
+        grad = torch.empty((rows, hidden), dtype=torch.bfloat16, device=g.device)
+    if dot is None:
+        dot = torch.empty((rows,), dtype=torch.float32, device=g.device)
+    _need(grad, "grad", torch.bfloat16, 2)
+    _need(dot, "dot", torch.float32, 1)
+    if tuple(grad.shape) != (rows, hidden) or dot.shape[0] != rows:
+        raise ValueError("grad must be [rows, hidden] and dot [rows]")
+    _check(library().rd_unsort_bwd_rows(_ptr(g), _ptr(y), _ptr(w), _ptr(limit), _ptr(grad), _ptr(dot), rows, hidden,
+                                        _stream(stream)))
+    return grad, dot

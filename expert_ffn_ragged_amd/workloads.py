@@ -29,7 +29,7 @@ import torch
 _CHUNK = 1 << 26  # elements per float32 generation chunk
 
 # Tensor ids inside a workload, used to derive per-tensor seeds.
-_X, _W, _DY, _FUSED, _DOUT = 1, 2, 3, 4, 5
+_X, _W, _DY, _FUSED, _DOUT, _UG, _UY, _UW = 1, 2, 3, 4, 5, 6, 7, 8
 
 WORKLOADS = {
     1: dict(name="tiny m256 k128 n256 g4", m=256, k=128, n=256, G=4),
@@ -106,11 +106,26 @@ def bf16_normal(shape, std, seed, device="cpu", nan_rows_from=None):
     return out
 
 
+def f32_uniform(n, lo, hi, seed, device="cpu", nan_from=None):
+    """float32 tensor of U[lo, hi) draws from its own generator; entries ``>= nan_from`` hold NaN."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    out = torch.rand(int(n), generator=gen, device=device, dtype=torch.float32)
+    out.mul_(hi - lo).add_(lo)
+    if nan_from is not None and nan_from < n:
+        out[nan_from:] = float("nan")
+    return out
+
+
 def make(workload, device="cpu", parts=("x", "w", "dy"), seed=None):
     """Inputs of one workload as a dict of tensors (bf16 on ``device``; ``gs`` int32 on ``device``).
 
     Keys: ``gs`` (and ``gs_host``), plus the requested parts among
     ``x``, ``w``, ``dy``, ``fused``, ``d_out``, and the scalars of the workload.
+    Workload 4 also offers the weighted-unsort-backward inputs: ``ug`` (the
+    gathered gradient) and ``uy`` (the expert outputs), both ``[m, k]`` bf16
+    N(0, 1), and ``uw`` (routing weights, ``[m]`` float32 U[-1, 1)), all NaN
+    past the limit.
     """
     cfg = dict(WORKLOADS[workload])
     base = 1000 * (workload if seed is None else seed)
@@ -156,6 +171,12 @@ def make(workload, device="cpu", parts=("x", "w", "dy"), seed=None):
             d["fused"] = bf16_normal((m, 2 * n), 1.0, base + _FUSED, device, nan_rows_from=limit)
         if "d_out" in parts:
             d["d_out"] = bf16_normal((m, n), 1.0, base + _DOUT, device, nan_rows_from=limit)
+        if "ug" in parts:
+            d["ug"] = bf16_normal((m, k), 1.0, base + _UG, device, nan_rows_from=limit)
+        if "uy" in parts:
+            d["uy"] = bf16_normal((m, k), 1.0, base + _UY, device, nan_rows_from=limit)
+        if "uw" in parts:
+            d["uw"] = f32_uniform(m, -1.0, 1.0, base + _UW, device, nan_from=limit)
         return d
     if workload == 5:
         if "x" in parts:

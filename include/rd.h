@@ -9,7 +9,8 @@
  *             group_offset window of the suggested fast_ragged_dot.
  *   [MaxText] MaxText PR #5760, "397B v7x trainer: MoE wo FSDP sharding and
  *             valid-rows-only MoE kernels", commit on valid rows: the
- *             packed-buffer row limit and the glu_rows forward/backward.
+ *             packed-buffer row limit, the glu_rows forward/backward and the
+ *             weighted unsort backward (unsort_bwd_rows).
  *   [TE]      TransformerEngine PR #2213, "Async issuing D2H memcpy for
  *             grouped_gemm group_sizes array", Description: copying
  *             group_sizes to the host stalls the GPU and breaks graph capture.
@@ -183,6 +184,29 @@ int rd_glu_fwd(const void* fused, const int32_t* limit, void* out, int64_t rows,
  */
 int rd_glu_bwd(const void* fused, const void* d_out, const int32_t* limit, void* d_fused,
                int64_t rows, int64_t h, void* stream);
+
+/*
+ * Weighted unsort backward over the valid rows ([MaxText], unsort_bwd_rows:
+ * the buffered branch of the ring unsort backward).
+ *
+ *   g     [rows, hidden] bf16: the incoming gradient gathered into the packed
+ *         expert buffer's (sorted) row order.
+ *   y     [rows, hidden] bf16: the expert outputs in the same order.
+ *   w     [rows] float32: each row's routing weight.
+ *   limit NULL (all rows) or [1] int32 on the device.
+ *   grad  [rows, hidden] bf16: grad[r, c] = bf16(f32(g[r, c]) * w[r]), a
+ *         float32 product rounded once to bf16 (RNE).
+ *   dot   [rows] float32: dot[r] = sum_c f32(g[r, c]) * f32(y[r, c]), the
+ *         routing-weight gradient, summed in float32 in a fixed order (the
+ *         same on every run; the page leaves the order free).
+ *
+ * Rows r >= L = clamp(*limit, 0, rows) are neither read nor written (in any
+ * of the five arrays).  hidden > 0 and a multiple of 8; g, y, grad 16-byte
+ * aligned; w, dot 4-byte aligned.  With rows == 0 nothing is launched and the
+ * pointers may be NULL.
+ */
+int rd_unsort_bwd_rows(const void* g, const void* y, const float* w, const int32_t* limit, void* grad, float* dot,
+                       int64_t rows, int64_t hidden, void* stream);
 
 #ifdef __cplusplus
 }

@@ -108,3 +108,24 @@ def test_forward_workspace_size_follows_the_decode_rule(lib):
     assert lib.rd_forward_workspace_size(512, 4096, 136, 128, 0) == 0       # n: no 256-column strips
     assert lib.rd_forward_workspace_size(512, 12, 1536, 128, 0) == 0        # invalid k
     assert lib.rd_forward_workspace_size(512, 4096, 1536, 0, 0) == 0        # invalid num_local
+
+
+def test_unsort_rejects_bad_arguments(lib):
+    v = ctypes.c_void_p
+    ok = dict(g=16, y=16, w=16, limit=None, grad=16, dot=16, rows=4, hidden=8)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        p = lambda x: None if x is None else v(x)
+        return lib.rd_unsort_bwd_rows(p(a["g"]), p(a["y"]), p(a["w"]), p(a["limit"]), p(a["grad"]), p(a["dot"]),
+                                      a["rows"], a["hidden"], None)
+    assert call(hidden=12) == rd.RD_EUNSUPPORTED
+    assert call(hidden=0) == rd.RD_EINVAL
+    assert call(rows=-1) == rd.RD_EINVAL
+    assert call(g=None) == rd.RD_EINVAL
+    assert call(dot=None) == rd.RD_EINVAL
+    assert call(grad=24) == rd.RD_EINVAL       # misaligned
+    assert call(w=18) == rd.RD_EINVAL          # misaligned float
+    assert call(limit=18) == rd.RD_EINVAL      # misaligned int32
+    assert call(rows=0, g=None, y=None, w=None, grad=None, dot=None) == rd.RD_OK
