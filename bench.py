@@ -223,7 +223,36 @@ def extra_all(steps):
     out["window_limit_unsort_bwd_rows"] = {"ms": round(per["unsort"], 4), "GB/s": round(nbytes / per["unsort"] / 1e6, 1),
                                            "hbm_frac": round(nbytes / per["unsort"] / 1e6 / HBM_PEAK_GBS, 4),
                                            "algorithmic_bytes": int(nbytes)}
+    del d, grad, dot
+    torch.cuda.empty_cache()
+    out.update(mlp_layer(steps))
     return out
+
+
+def mlp_layer(steps):
+    """The whole MoE expert MLP through the autograd wrapper, forward and backward: wi [64, 4096, 2048]
+    as [gate | up], GLU, wo [64, 1024, 4096], on the up-projection's 8192 rows and Zipf(1.1) sizes."""
+    import torch
+
+    from expert_ffn_ragged_amd import autograd as ag
+    from expert_ffn_ragged_amd import workloads
+
+    d = workloads.make(2, "cuda", parts=("x", "w"))
+    x = d["x"].requires_grad_(True)
+    wi = d["w"].requires_grad_(True)
+    wo = workloads.bf16_normal((64, 1024, 4096), 0.02, 2007, "cuda").requires_grad_(True)
+    dout = workloads.bf16_normal((d["m"], 4096), 1.0, 2008, "cuda")
+    rows = int(d["gs_host"].sum())
+
+    def step():
+        out = ag.moe_mlp(x, wi, wo, d["gs"])
+        torch.autograd.grad(out, (x, wi, wo), dout)
+
+    _, _, per = timed_ops([("mlp", step)], steps, 3)
+    flop = 3 * (2.0 * rows * 4096 * 2048 + 2.0 * rows * 1024 * 4096)
+    return {"moe_mlp_fwd_bwd_m8192_d4096_h1024_g64": {"ms": round(per["mlp"], 4),
+                                                     "TFLOP/s": round(flop / per["mlp"] / 1e9, 1),
+                                                     "mfma_frac": round(flop / per["mlp"] / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}}
 
 
 def cpu_baseline(x, w, dy, gs_host, budget_s=12.0):
