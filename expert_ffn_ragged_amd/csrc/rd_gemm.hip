@@ -787,7 +787,10 @@ struct StreamOps<kTransTN, BM, BN, KS> {
 // wave that slot (g-1) % S is free, and the producer refills it.  A tile's
 // epilogue stages its bf16 results in the slot of its last step.
 // WGS workgroups share a CU (1, or 2 for the small-ring variant).
-template <int MODE, int BM, int BN, int S, int KS, int WGS>
+// MAXL bounds num_local for the LDS schedule arrays (a smaller bound frees
+// LDS for a deeper ring; the host only picks such a variant when num_local
+// fits).
+template <int MODE, int BM, int BN, int S, int KS, int WGS, int MAXL = RD_MAX_GROUPS>
 __global__ __launch_bounds__(kThreads, WGS) void grouped_gemm_stream(KArgs p) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int MI = WM / 32, NI = WN / 32;
@@ -800,8 +803,8 @@ __global__ __launch_bounds__(kThreads, WGS) void grouped_gemm_stream(KArgs p) {
   using Tiles = typename std::conditional<MODE == kTransTN, TransTiles, FwdTiles>::type;
   constexpr int L = OpA::kInstr + OpB::kInstr;  // loads per wave per step
   __shared__ __attribute__((aligned(1024))) uint16_t s_tiles[S * ST];
-  __shared__ int s_lb[RD_MAX_GROUPS + 1];
-  __shared__ int s_aux[RD_MAX_GROUPS + 1];
+  __shared__ int s_lb[MAXL + 1];
+  __shared__ int s_aux[MAXL + 1];
   __shared__ long long s_wave[kThreads / 64];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1157,9 +1160,10 @@ int grid_size(long long work_items, int per_cu) {
 // shape runs 4 waves in a 2 x 2 layout; larger wave tiles read fewer LDS bytes
 // per MFMA, smaller BM wastes fewer MFMA rows on short groups.
 enum Tile { kT64x128 = 0, kT128x128 = 1, kT128x256 = 2, kT256x256 = 3, kT128x128x2 = 4, kT64x64 = 5, kT256x256k32 = 6,
-            kT128x256k32 = 7, kT128x256x2 = 8, kT128x128k32x2 = 9, kTileCount };
+            kT128x256k32 = 7, kT128x256x2 = 8, kT128x128k32x2 = 9, kT128x128x3 = 10, kT256x128x2 = 11,
+            kT128x256s3x2 = 12, kTileCount };
 
-// RD_FWD_TILE / RD_TRANS_TILE (0..9) force a shape, for tile sweeps.
+// RD_FWD_TILE / RD_TRANS_TILE (0..12) force a shape, for tile sweeps.
 int forced_tile(const char* name) {
   const char* v = getenv(name);
   if (v == nullptr || *v == 0) return -1;
@@ -1170,38 +1174,36 @@ int forced_tile(const char* name) {
 // Forward shape from what the host knows (never the device-resident group
 // sizes): m / num_local bounds the mean rows per local group.  Decode-sized
 // groups take a 64-row tile (when no workspace allows the split-contraction
-// path); groups of up to 256 rows on average take 128 x 256 tiles with two
-// workgroups per CU (one multiplies while the other drains its stores);
-// longer groups take 128 x 256 with one workgroup and a 3-stage ring, as does
-// every trans_rhs call.  Chosen from sweeps of every shape on the
-// up-projection, backward, window+limit and decode workloads.
+// path); otherwise 128 x 256 tiles with two workgroups per CU (one
+// multiplies while the other drains its stores), with a 3-slot ring for long
+// groups; trans_rhs calls take one workgroup per CU with a 3 x 64-deep ring.
+// Chosen from sweeps of every shape on the up-projection, backward,
+// window+limit and decode workloads.
 int pick_forward_tile(const GemmProblem& p, bool trans_rhs) {
   const int forced = forced_tile("RD_FWD_TILE");
   if (forced >= 0) return forced;
   const long long avg_rows = p.m / (p.num_local > 0 ? p.num_local : 1);
   if (avg_rows <= 48) return kT64x128;
   if (p.n < 256) return kT128x128;
-  return !trans_rhs && avg_rows <= 256 ? kT128x256x2 : kT128x256;
+  if (trans_rhs) return kT128x256;
+  return avg_rows <= 256 ? kT128x256x2 : kT128x256s3x2;
 }
 
-// trans_ragged_dot: the contraction runs over a group's rows.  Short groups
-// (at most 256 rows on average) make the kernel a stream of dW writes; two
-// co-resident 128 x 256 workgroups per CU overlap one's stores with the
-// other's multiplies.  Longer groups do best with two 128 x 128 workgroups
-// per CU and 64-deep stages.
+// trans_ragged_dot: the contraction runs over a group's rows.  Two
+// co-resident 128 x 256 workgroups per CU with 3-slot rings of 32-deep stages
+// (one workgroup multiplies while the other drains its dW stores).
 int pick_trans_tile(const GemmProblem& p) {
   const int forced = forced_tile("RD_TRANS_TILE");
   if (forced >= 0) return forced;
-  const long long avg_rows = p.m / (p.num_local > 0 ? p.num_local : 1);
-  return avg_rows <= 256 && p.k >= 128 && p.n >= 256 ? kT128x256x2 : kT128x128x2;
+  return p.k >= 128 && p.n >= 256 ? kT128x256s3x2 : kT128x128x2;
 }
 
-template <int MODE, int BM, int BN, int S, int KS = 32, int WGS = 1>
+template <int MODE, int BM, int BN, int S, int KS = 32, int WGS = 1, int MAXL = RD_MAX_GROUPS>
 void launch_one(const KArgs& a, long long work, hipStream_t stream) {
   if constexpr (S == 0)
     grouped_gemm_regs<MODE, BM, BN><<<grid_size(work, 2), kThreads, 0, stream>>>(a);
   else
-    grouped_gemm_stream<MODE, BM, BN, S, KS, WGS><<<grid_size(work, WGS), kThreads, 0, stream>>>(a);
+    grouped_gemm_stream<MODE, BM, BN, S, KS, WGS, MAXL><<<grid_size(work, WGS), kThreads, 0, stream>>>(a);
 }
 
 template <int MODE>
@@ -1225,6 +1227,14 @@ void launch_tile(int tile, const KArgs& a, const GemmProblem& p, hipStream_t str
     case kT128x256k32: launch_one<MODE, 128, 256, 6, 32>(a, work(128, 256), stream); break;
     case kT128x256x2: launch_one<MODE, 128, 256, 2, 32, 2>(a, work(128, 256), stream); break;
     case kT128x128k32x2: launch_one<MODE, 128, 128, 3, 32, 2>(a, work(128, 128), stream); break;
+    case kT128x128x3: launch_one<MODE, 128, 128, 2, 32, 3>(a, work(128, 128), stream); break;
+    case kT256x128x2: launch_one<MODE, 256, 128, 2, 32, 2>(a, work(256, 128), stream); break;
+    case kT128x256s3x2:  // a 3-slot ring for two workgroups per CU fits only with num_local <= 512
+      if (p.num_local <= 512)
+        launch_one<MODE, 128, 256, 3, 32, 2, 512>(a, work(128, 256), stream);
+      else
+        launch_one<MODE, 128, 256, 2, 32, 2>(a, work(128, 256), stream);
+      break;
     default: launch_one<MODE, 128, 128, 4, 64>(a, work(128, 128), stream); break;
   }
 }
