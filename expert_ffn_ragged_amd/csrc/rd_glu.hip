@@ -7,13 +7,22 @@
 // + 1, divide, multiply in float32 and rounds only the output; the backward
 // writes [d_gate | d_up] in one pass and maps -0 to +0.
 //
-// This translation unit is compiled with -ffp-contract=off (no FMA
-// contraction) and without fast-math: '/' is IEEE correctly rounded, expf is
-// the device library's accurate exp, and float32 denormals are preserved.
+// Arithmetic: float32, in the page's op order, compiled with
+// -ffp-contract=off (no FMA contraction) and without fast-math, denormals
+// kept.  exp(-g) is the hardware base-2 exponential of -g * log2(e), and a
+// divide by den = 1 + exp(-g) is a multiply by the hardware reciprocal; when
+// den > 2^64 the reciprocal is taken of den * 2^-64 and the product scaled
+// back by 2^-64, so the reciprocal stays in the normal range where the
+// hardware keeps its accuracy (den reaches 2^128 or inf) and a denormal
+// result is rounded once, by the final scaling.  The error is within about
+// 2^-16 relative of the exact value (the rounding of -g * log2(e) dominates,
+// |g| <= 89), far inside the 2^-9 of a bf16 half-ulp, so every output is
+// within one bf16 ulp of the correctly rounded float32 evaluation.  Special values follow the op
+// sequence: g = -inf gives NaN, exp overflow gives -0, g = +inf gives inf.
 //
-// Both kernels are HBM-bound streams: a persistent grid walks 16-byte chunks
-// (8 bf16) of the valid rows with 128-bit loads and stores, two chunks per
-// thread per iteration to keep more bytes in flight.
+// Both kernels are HBM-bound streams: a persistent grid of waves walks the
+// valid rows, one wave per row, with 128-bit non-temporal loads and stores of
+// 16-byte chunks (8 bf16; the data is touched once).
 #include "rd_device.h"
 #include "rd_launch.h"
 
@@ -28,14 +37,40 @@ __device__ __forceinline__ int clamp_limit(const int32_t* limp, int rows) {
   return v < 0 ? 0 : (v > rows ? rows : v);
 }
 
+constexpr float kLog2e = 1.44269504088896341f;
+constexpr float kTwoM64 = 5.42101086242752217e-20f;  // 2^-64
+constexpr float kTwo64 = 1.8446744073709551616e19f;  // 2^64
+
+typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
+
+// 128-bit loads and stores marked non-temporal (streamed once, not kept in cache).
+__device__ __forceinline__ uint4 nt_load(const uint16_t* p) {
+  const nt_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void nt_store(uint16_t* p, uint4 v) {
+  const nt_u32x4 x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<nt_u32x4*>(p));
+}
+
+// den = 1 + exp(-g); x / den as (x * rcp(den * sc)) * sc with sc = 2^-64
+// when den > 2^64 (then g < -44, so x * rcp stays finite) and sc = 1 otherwise.
+struct ScaledRcp {
+  float r, sc;
+};
+__device__ __forceinline__ ScaledRcp rcp_den(float g) {
+  const float den = __builtin_amdgcn_exp2f(-g * kLog2e) + 1.0f;
+  const float sc = den > kTwo64 ? kTwoM64 : 1.0f;
+  return ScaledRcp{__builtin_amdgcn_rcpf(den * sc), sc};
+}
+__device__ __forceinline__ float div_den(float x, const ScaledRcp& q) { return (x * q.r) * q.sc; }
+
 __device__ __forceinline__ float lo16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // silu(g) * u in the page's op order: negate, exp, + 1, divide, multiply.
 __device__ __forceinline__ float glu_f32(float g, float u) {
-  const float e = expf(-g);
-  const float den = e + 1.0f;
-  const float s = g / den;
+  const float s = div_den(g, rcp_den(g));
   return s * u;
 }
 
@@ -56,10 +91,9 @@ __device__ __forceinline__ uint32_t no_negzero(uint32_t w) {
 
 // Backward of one element: d_gate and d_up as float32, in a fixed op order.
 __device__ __forceinline__ void glu_grad_f32(float g, float u, float d, float& d_gate, float& d_up) {
-  const float e = expf(-g);
-  const float den = e + 1.0f;
-  const float sig = 1.0f / den;
-  const float silu = g / den;
+  const ScaledRcp q = rcp_den(g);
+  const float sig = div_den(1.0f, q);
+  const float silu = div_den(g, q);
   d_up = d * silu;
   d_gate = ((d * u) * sig) * (1.0f + g * (1.0f - sig));
 }
@@ -72,50 +106,44 @@ __device__ __forceinline__ void glu_grad_word(uint32_t gw, uint32_t uw, uint32_t
   ouw = no_negzero(pack_bf16x2(u0, u1));
 }
 
+// One wave per row: lane l takes the row's 16-byte chunks l, l + 64, ...
+// (two per iteration); rows are strided over all waves of the grid.  No
+// division per chunk.
 __global__ __launch_bounds__(kThreads) void glu_fwd_kernel(const uint16_t* __restrict__ fused,
                                                            const int32_t* __restrict__ limp,
                                                            uint16_t* __restrict__ out, int rows, int h) {
   const int L = clamp_limit(limp, rows);
   const int hc = h >> 3;  // 16-byte chunks per output row
-  const long long total = static_cast<long long>(L) * hc;
-  const long long stride = static_cast<long long>(gridDim.x) * kThreads;
-  long long q = static_cast<long long>(blockIdx.x) * kThreads + threadIdx.x;
-  for (; q + stride < total; q += 2 * stride) {
-    const long long q1 = q + stride;
-    const int r0 = static_cast<int>(q / hc), c0 = static_cast<int>(q - static_cast<long long>(r0) * hc);
-    const int r1 = static_cast<int>(q1 / hc), c1 = static_cast<int>(q1 - static_cast<long long>(r1) * hc);
-    const uint16_t* f0 = fused + static_cast<long long>(r0) * 2 * h + c0 * 8;
-    const uint16_t* f1 = fused + static_cast<long long>(r1) * 2 * h + c1 * 8;
-    const uint4 g0 = *reinterpret_cast<const uint4*>(f0);
-    const uint4 u0 = *reinterpret_cast<const uint4*>(f0 + h);
-    const uint4 g1 = *reinterpret_cast<const uint4*>(f1);
-    const uint4 u1 = *reinterpret_cast<const uint4*>(f1 + h);
-    *reinterpret_cast<uint4*>(out + static_cast<long long>(r0) * h + c0 * 8) = glu_chunk(g0, u0);
-    *reinterpret_cast<uint4*>(out + static_cast<long long>(r1) * h + c1 * 8) = glu_chunk(g1, u1);
-  }
-  if (q < total) {
-    const int r0 = static_cast<int>(q / hc), c0 = static_cast<int>(q - static_cast<long long>(r0) * hc);
-    const uint16_t* f0 = fused + static_cast<long long>(r0) * 2 * h + c0 * 8;
-    const uint4 g0 = *reinterpret_cast<const uint4*>(f0);
-    const uint4 u0 = *reinterpret_cast<const uint4*>(f0 + h);
-    *reinterpret_cast<uint4*>(out + static_cast<long long>(r0) * h + c0 * 8) = glu_chunk(g0, u0);
+  const int lane = threadIdx.x & 63;
+  const int waves = gridDim.x * (kThreads / 64);
+  for (int r = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); r < L; r += waves) {
+    const uint16_t* f = fused + static_cast<long long>(r) * 2 * h;
+    uint16_t* o = out + static_cast<long long>(r) * h;
+    int c = lane;
+    for (; c + 64 < hc; c += 128) {
+      const uint4 g0 = nt_load(f + c * 8);
+      const uint4 u0 = nt_load(f + h + c * 8);
+      const uint4 g1 = nt_load(f + (c + 64) * 8);
+      const uint4 u1 = nt_load(f + h + (c + 64) * 8);
+      nt_store(o + c * 8, glu_chunk(g0, u0));
+      nt_store(o + (c + 64) * 8, glu_chunk(g1, u1));
+    }
+    if (c < hc) nt_store(o + c * 8, glu_chunk(nt_load(f + c * 8), nt_load(f + h + c * 8)));
   }
 }
 
-__device__ __forceinline__ void glu_bwd_one(const uint16_t* __restrict__ fused, const uint16_t* __restrict__ d_out,
-                                            uint16_t* __restrict__ d_fused, long long q, int hc, int h) {
-  const int r = static_cast<int>(q / hc), c = static_cast<int>(q - static_cast<long long>(r) * hc);
-  const long long frow = static_cast<long long>(r) * 2 * h + c * 8;
-  const uint4 g = *reinterpret_cast<const uint4*>(fused + frow);
-  const uint4 u = *reinterpret_cast<const uint4*>(fused + frow + h);
-  const uint4 d = *reinterpret_cast<const uint4*>(d_out + static_cast<long long>(r) * h + c * 8);
+__device__ __forceinline__ void glu_bwd_chunk(const uint16_t* __restrict__ f, const uint16_t* __restrict__ d,
+                                              uint16_t* __restrict__ df, int c, int h) {
+  const uint4 g = nt_load(f + c * 8);
+  const uint4 u = nt_load(f + h + c * 8);
+  const uint4 dv = nt_load(d + c * 8);
   uint4 og, ou;
-  glu_grad_word(g.x, u.x, d.x, og.x, ou.x);
-  glu_grad_word(g.y, u.y, d.y, og.y, ou.y);
-  glu_grad_word(g.z, u.z, d.z, og.z, ou.z);
-  glu_grad_word(g.w, u.w, d.w, og.w, ou.w);
-  *reinterpret_cast<uint4*>(d_fused + frow) = og;
-  *reinterpret_cast<uint4*>(d_fused + frow + h) = ou;
+  glu_grad_word(g.x, u.x, dv.x, og.x, ou.x);
+  glu_grad_word(g.y, u.y, dv.y, og.y, ou.y);
+  glu_grad_word(g.z, u.z, dv.z, og.z, ou.z);
+  glu_grad_word(g.w, u.w, dv.w, og.w, ou.w);
+  nt_store(df + c * 8, og);
+  nt_store(df + h + c * 8, ou);
 }
 
 __global__ __launch_bounds__(kThreads) void glu_bwd_kernel(const uint16_t* __restrict__ fused,
@@ -124,16 +152,20 @@ __global__ __launch_bounds__(kThreads) void glu_bwd_kernel(const uint16_t* __res
                                                            uint16_t* __restrict__ d_fused, int rows, int h) {
   const int L = clamp_limit(limp, rows);
   const int hc = h >> 3;
-  const long long total = static_cast<long long>(L) * hc;
-  const long long stride = static_cast<long long>(gridDim.x) * kThreads;
-  for (long long q = static_cast<long long>(blockIdx.x) * kThreads + threadIdx.x; q < total; q += stride)
-    glu_bwd_one(fused, d_out, d_fused, q, hc, h);
+  const int lane = threadIdx.x & 63;
+  const int waves = gridDim.x * (kThreads / 64);
+  for (int r = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); r < L; r += waves) {
+    const long long fo = static_cast<long long>(r) * 2 * h;
+    const uint16_t* d = d_out + static_cast<long long>(r) * h;
+    for (int c = lane; c < hc; c += 64) glu_bwd_chunk(fused + fo, d, d_fused + fo, c, h);
+  }
 }
 
-int elementwise_grid(int rows, int h) {
-  const long long chunks = static_cast<long long>(rows) * (h / 8);
-  const long long blocks = (chunks + kThreads - 1) / kThreads;
-  const long long cap = static_cast<long long>(device_cu_count()) * 8;
+// A wave per row, at most per_cu workgroups per CU.
+int elementwise_grid(int rows, int h, int per_cu) {
+  (void)h;
+  const long long blocks = (static_cast<long long>(rows) + kThreads / 64 - 1) / (kThreads / 64);
+  const long long cap = static_cast<long long>(device_cu_count()) * per_cu;
   const long long g = blocks < cap ? blocks : cap;
   return static_cast<int>(g < 1 ? 1 : g);
 }
@@ -141,14 +173,14 @@ int elementwise_grid(int rows, int h) {
 }  // namespace
 
 int launch_glu_fwd(const void* fused, const int32_t* limit, void* out, int rows, int h, hipStream_t stream) {
-  glu_fwd_kernel<<<elementwise_grid(rows, h), kThreads, 0, stream>>>(static_cast<const uint16_t*>(fused), limit,
+  glu_fwd_kernel<<<elementwise_grid(rows, h, 32), kThreads, 0, stream>>>(static_cast<const uint16_t*>(fused), limit,
                                                                        static_cast<uint16_t*>(out), rows, h);
   return hipGetLastError() == hipSuccess ? RD_OK : RD_EHIP;
 }
 
 int launch_glu_bwd(const void* fused, const void* d_out, const int32_t* limit, void* d_fused, int rows, int h,
                    hipStream_t stream) {
-  glu_bwd_kernel<<<elementwise_grid(rows, h), kThreads, 0, stream>>>(
+  glu_bwd_kernel<<<elementwise_grid(rows, h, 32), kThreads, 0, stream>>>(
       static_cast<const uint16_t*>(fused), static_cast<const uint16_t*>(d_out), limit,
       static_cast<uint16_t*>(d_fused), rows, h);
   return hipGetLastError() == hipSuccess ? RD_OK : RD_EHIP;

@@ -162,10 +162,12 @@ int rd_trans(const void* x, const void* dy, const int32_t* group_sizes, int32_t 
  *   limit NULL (all rows) or [1] int32 on the device.
  *
  * For r < L: out[r,c] = bf16(g / (1 + exp(-g)) * u), g = fused[r,c],
- * u = fused[r,h+c], evaluated in float32 in exactly that order (negate, exp,
- * +1, divide, multiply) with a correctly rounded divide, the device exp, no
- * denormal flushing and no contraction into FMA; only the result is rounded
- * (RNE).  Rows >= L are neither read nor written.  h > 0, multiple of 8.
+ * u = fused[r,h+c], evaluated in float32 in that order (negate, exp, +1,
+ * divide, multiply), no denormal flushing and no contraction into FMA; only
+ * the result is rounded (RNE).  exp and the divide use the hardware base-2
+ * exponential and (range-scaled) reciprocal, which keeps every output within
+ * one bf16 ulp of the correctly rounded float32 evaluation.  Rows >= L are neither read nor written.
+ * h > 0, multiple of 8.
  */
 int rd_glu_fwd(const void* fused, const int32_t* limit, void* out, int64_t rows, int64_t h,
                void* stream);
@@ -179,7 +181,8 @@ int rd_glu_fwd(const void* fused, const int32_t* limit, void* out, int64_t rows,
  * For r < L, in float32 with s = 1 / (1 + exp(-g)):
  *   d_up   = d * (g / (1 + exp(-g)))
  *   d_gate = ((d * u) * s) * (1 + g * (1 - s))
- * each rounded once (RNE), then -0 is written as +0 in both halves.
+ * each rounded once (RNE), then -0 is written as +0 in both halves; exp and
+ * the divides as in rd_glu_fwd (within one bf16 ulp).
  * Rows >= L are neither read nor written.  h > 0, multiple of 8.
  */
 int rd_glu_bwd(const void* fused, const void* d_out, const int32_t* limit, void* d_fused,
