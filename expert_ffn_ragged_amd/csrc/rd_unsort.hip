@@ -9,12 +9,12 @@
 // free.  Rows at or past the limit are neither read nor written.
 //
 // One wave64 owns a row: lane l handles the 16-byte chunks l, l + 64, ... of
-// it (128-bit loads of g and y, 128-bit stores of the gradient, four chunks
-// in flight per lane), keeps its part of the dot in float32, and the wave
-// adds the 64 parts in a fixed butterfly order.  A row's dot is therefore
+// it (128-bit non-temporal loads of g and y and stores of the gradient, four
+// chunks in flight per lane), keeps its part of the dot in float32, and the
+// wave adds the 64 parts in a fixed butterfly order.  A row's dot is therefore
 // produced by exactly one wave: no partial sums cross workgroups, no atomics,
-// and the result is the same on every run.  A persistent grid of waves
-// strides over the valid rows.  HBM-bound: 3 * 2 * hidden + 8 bytes per row.
+// and the result is the same on every run.  A persistent grid of waves (32
+// workgroups per CU) strides over the valid rows.  HBM-bound: 3 * 2 * hidden + 8 bytes per row.
 #include "rd_device.h"
 #include "rd_launch.h"
 
@@ -22,6 +22,18 @@ namespace rd {
 namespace {
 
 constexpr int kUnroll = 4;  // 16-byte chunks per lane in flight
+
+typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
+
+// 128-bit loads and stores marked non-temporal (every byte is touched once).
+__device__ __forceinline__ uint4 nt_load(const uint4* p) {
+  const nt_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void nt_store(uint4* p, uint4 v) {
+  const nt_u32x4 x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<nt_u32x4*>(p));
+}
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -64,13 +76,13 @@ __global__ __launch_bounds__(kThreads) void unsort_bwd_rows_kernel(const uint16_
       uint4 gv[kUnroll], yv[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        gv[u] = gr[c + 64 * u];
-        yv[u] = yr[c + 64 * u];
+        gv[u] = nt_load(gr + c + 64 * u);
+        yv[u] = nt_load(yr + c + 64 * u);
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        dr[c + 64 * u] = make_uint4(grad_word(gv[u].x, wr), grad_word(gv[u].y, wr), grad_word(gv[u].z, wr),
-                                    grad_word(gv[u].w, wr));
+        nt_store(dr + c + 64 * u, make_uint4(grad_word(gv[u].x, wr), grad_word(gv[u].y, wr),
+                                             grad_word(gv[u].z, wr), grad_word(gv[u].w, wr)));
         acc = dot_word(gv[u].x, yv[u].x, acc);
         acc = dot_word(gv[u].y, yv[u].y, acc);
         acc = dot_word(gv[u].z, yv[u].z, acc);
@@ -78,8 +90,9 @@ __global__ __launch_bounds__(kThreads) void unsort_bwd_rows_kernel(const uint16_
       }
     }
     for (; c < chunks; c += 64) {
-      const uint4 gv = gr[c], yv = yr[c];
-      dr[c] = make_uint4(grad_word(gv.x, wr), grad_word(gv.y, wr), grad_word(gv.z, wr), grad_word(gv.w, wr));
+      const uint4 gv = nt_load(gr + c), yv = nt_load(yr + c);
+      nt_store(dr + c,
+               make_uint4(grad_word(gv.x, wr), grad_word(gv.y, wr), grad_word(gv.z, wr), grad_word(gv.w, wr)));
       acc = dot_word(gv.x, yv.x, acc);
       acc = dot_word(gv.y, yv.y, acc);
       acc = dot_word(gv.z, yv.z, acc);
@@ -97,7 +110,7 @@ int launch_unsort_bwd_rows(const void* g, const void* y, const float* w, const i
                            float* dot, int rows, int hidden, hipStream_t stream) {
   const long long waves_needed = rows;
   long long blocks = (waves_needed + (kThreads / 64) - 1) / (kThreads / 64);
-  const long long cap = static_cast<long long>(device_cu_count()) * 8;
+  const long long cap = static_cast<long long>(device_cu_count()) * 32;
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   unsort_bwd_rows_kernel<<<static_cast<int>(blocks), kThreads, 0, stream>>>(
