@@ -226,6 +226,15 @@ __device__ __forceinline__ void dma16(u32x4_t r, uint32_t lds_addr, uint32_t vof
                : "memory");
 }
 
+// The same load marked non-temporal, for data read exactly once (the decode
+// path's weight stream): it does not displace reused lines from the caches.
+__device__ __forceinline__ void dma16_nt(u32x4_t r, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(r), "s"(soff)
+               : "memory");
+}
+
 // Scalar operands of dma16 are wave-uniform by construction; readfirstlane
 // states it, so the compiler keeps them in SGPRs as the instruction needs.
 __device__ __forceinline__ uint32_t uniform(uint32_t v) {
@@ -1021,7 +1030,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_streamk_gemm(KArgs p, floa
     if (lane < 16) dma16(ra, slot + wave * 256, va, uniform(static_cast<uint32_t>(kr) * 2));
     const uint32_t sb = uniform(static_cast<uint32_t>(kr) * p.n * 2);
 #pragma unroll
-    for (int q = 0; q < BI; ++q) dma16(rb, slot + A_BYTES + (wave * BI + q) * 1024, vb[q], sb);
+    for (int q = 0; q < BI; ++q) dma16_nt(rb, slot + A_BYTES + (wave * BI + q) * 1024, vb[q], sb);
     ++p_kt;
     ++issued;
   };
