@@ -56,3 +56,44 @@ def test_decode_layer_graph_replays_follow_device_group_sizes():
         assert torch.equal(got.view(torch.int16), y2.view(torch.int16)), f"replay {i} differs from eager"
         if sizes.sum() == 0:
             assert bool((got.view(torch.int16) == 0).all())
+
+
+def test_moe_mlp_training_step_graph_replays_follow_device_group_sizes():
+    """Forward and backward of the MoE MLP (autograd wrapper) captured in one graph."""
+    from expert_ffn_ragged_amd import autograd as ag
+
+    say("graph capture of the MoE MLP forward + backward")
+    G, m, d, h, dout_dim = 16, 1024, 512, 256, 384
+    gs = torch.from_numpy(workloads.random_sizes(G, m, seed=70, empty=(3,))).to(DEV)
+    x = bf16_normal((m, d), 1.0, 71, DEV).requires_grad_(True)
+    wi = bf16_normal((G, d, 2 * h), 0.05, 72, DEV).requires_grad_(True)
+    wo = bf16_normal((G, h, dout_dim), 0.06, 73, DEV).requires_grad_(True)
+    dout = bf16_normal((m, dout_dim), 1.0, 74, DEV)
+
+    def train_step():
+        out = ag.moe_mlp(x, wi, wo, gs)
+        return (out,) + torch.autograd.grad(out, (x, wi, wo), dout)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            train_step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        captured = train_step()
+
+    sizes = [workloads.random_sizes(G, m, seed=s, empty=e) for s, e in ((80, ()), (81, (0, 5)), (82, (15,)))]
+    sizes.append(np.array([m] + [0] * (G - 1), dtype=np.int32))
+    for i, sz in enumerate(sizes):
+        gs.copy_(torch.from_numpy(sz).to(DEV))  # a device-side rewrite, outside the graph
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in captured]
+        want = train_step()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("out", "dx", "dwi", "dwo"), got, want):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"replay {i}: {name} differs from eager"
