@@ -38,13 +38,33 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--all", action="store_true", help="also time the backward, window+limit and decode workloads")
+    ap.add_argument("--cold", action="store_true",
+                    help="flush L2 and the MALL (a 512 MiB write) before every timed step, outside the events")
     ap.add_argument("--copy-calib", action="store_true",
                     help="first copy 256 MiB device-to-device three times (reference kernel for HBM counters)")
     return ap.parse_args()
 
 
+PERCENTILES = {}  # op -> (p10, p50, p90) in ms, filled by timed_ops
+COLD = {"on": False, "buf": None}
+
+
+def flush_caches():
+    """Write a 512 MiB scratch buffer: evicts L2 and the 256 MB MALL before a cold iteration."""
+    import torch
+
+    if COLD["buf"] is None:
+        COLD["buf"] = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    COLD["buf"].fill_(1)
+
+
 def timed_ops(ops, steps, warmup):
-    """Run `warmup` untimed steps, then `steps` timed ones with per-op HIP events."""
+    """Run `warmup` untimed steps, then `steps` timed ones with per-op HIP events on the current stream.
+
+    With COLD on, the caches are flushed before every timed step, outside the events.
+    Returns (wall seconds, GPU ms from the first to the last event, {op: mean ms}); the
+    per-op p10/p50/p90 go to PERCENTILES.
+    """
     import torch
 
     for _ in range(warmup):
@@ -56,6 +76,8 @@ def timed_ops(ops, steps, warmup):
            for _ in range(steps)]
     t0 = time.perf_counter()
     for s in range(steps):
+        if COLD["on"]:
+            flush_caches()
         for (_, fn), (a, b) in zip(ops, evs[s]):
             a.record(stream)
             fn()
@@ -64,9 +86,14 @@ def timed_ops(ops, steps, warmup):
     wall = time.perf_counter() - t0
     per_op = {}
     for i, (name, _) in enumerate(ops):
-        per_op[name] = sum(evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(steps)) / steps
+        t = sorted(evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(steps))
+        per_op[name] = sum(t) / steps
+        q = lambda f: t[min(len(t) - 1, int(round(f * (len(t) - 1))))]
+        PERCENTILES[name] = (round(q(0.1), 4), round(q(0.5), 4), round(q(0.9), 4))
     first, last = evs[0][0][0], evs[-1][-1][1]
     gpu_ms = first.elapsed_time(last)
+    if COLD["on"]:  # the flushes sit between the events: the step is the sum of its ops
+        gpu_ms = sum(per_op.values()) * steps
     return wall, gpu_ms, per_op
 
 
@@ -158,7 +185,7 @@ def extra_workloads(steps):
     out["decode_m512_k4096_n1536_g128"] = {
         "ms": round(per["decode"], 4), "GB/s": round(nb / per["decode"] / 1e6, 1),
         "hbm_frac": round(nb / per["decode"] / 1e6 / HBM_PEAK_GBS, 4), "algorithmic_bytes": int(nb),
-        "traffic": None if t is None else int(t)}
+        "traffic": None if t is None else int(t), "p10_p50_p90_ms": PERCENTILES.get("decode")}
     del d, o
     torch.cuda.empty_cache()
     return out
@@ -312,6 +339,7 @@ def main():
     from expert_ffn_ragged_amd import rd
 
     rd.library()
+    COLD["on"] = args.cold
     if args.copy_calib:
         a = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
@@ -342,8 +370,10 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "pct_bf16_mfma_peak": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
         "roofline": roofline(dom, r["per_op"][dom], r["bytes"][dom], r["flops"][dom], traffic.get(dom)),
-        "per_kernel": {name: roofline(name, ms, r["bytes"][name], r["flops"][name], traffic.get(name))
+        "per_kernel": {name: dict(roofline(name, ms, r["bytes"][name], r["flops"][name], traffic.get(name)),
+                                  p10_p50_p90_ms=PERCENTILES.get(name))
                        for name, ms in r["per_op"].items()},
+        "timing": "cold (L2 and MALL flushed before each step)" if args.cold else "warm (inputs resident, caches warm)",
     }
     line["extra"] = extra_workloads(max(args.steps, 10))
     if args.all:
