@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, published (no sparsity)
+MFMA_FP8_PEAK_TFLOPS = 5033.2  # MI355X dense fp8 MFMA, published (no sparsity)
 METRIC = "ragged_dot TFLOP/s (valid rows) + % bf16 MFMA peak; decode-shape HBM GB/s"
 
 
@@ -198,6 +199,7 @@ def extra_all(steps):
 
     out = {}
     d = workloads.make(3, "cuda")
+    gs3 = d["gs"]
     m, k, n = d["m"], d["k"], d["n"]
     rows = int(d["gs_host"].sum())
     dx = torch.empty((m, k), dtype=torch.bfloat16, device="cuda")
@@ -212,7 +214,14 @@ def extra_all(steps):
     for key, ms in per.items():
         out[f"backward_m32768_{key}"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1),
                                         "mfma_frac": round(fl / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
-    del d, dx, dw, dw32
+    # the same dx with fp8 (E4M3) operands
+    dy8, w8 = d["dy"].to(torch.float8_e4m3fn), d["w"].to(torch.float8_e4m3fn)
+    del d, dw, dw32
+    torch.cuda.empty_cache()
+    _, _, per = timed_ops([("dx_fp8", lambda: rd.ragged_dot_fp8(dy8, w8, gs3, out=dx))], steps, 3)
+    out["backward_m32768_dx_fp8"] = {"ms": round(per["dx_fp8"], 4), "TFLOP/s": round(fl / per["dx_fp8"] / 1e9, 1),
+                                     "mfma_frac_fp8": round(fl / per["dx_fp8"] / 1e9 / MFMA_FP8_PEAK_TFLOPS, 4)}
+    del dy8, w8, dx
     torch.cuda.empty_cache()
     d = workloads.make(4, "cuda", parts=("x", "w", "fused", "d_out"))
     off = torch.tensor([96], dtype=torch.int32, device="cuda")

@@ -108,6 +108,39 @@ int rd_forward_trans_rhs(const void* x, const void* w, const int32_t* group_size
                         k, n, workspace, workspace_bytes, stream, true);
 }
 
+int rd_forward_trans_rhs_fp8(const void* x, const void* w, const int32_t* group_sizes, int32_t num_groups,
+                             const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* out,
+                             int32_t out_dtype, int64_t m, int64_t k, int64_t n, void* stream) {
+  int st = check_dims(m, k, n);
+  if (st != RD_OK) return st;
+  if ((k % 128) != 0) return RD_EUNSUPPORTED;
+  if (k * (m > n ? m : n) >= (int64_t(1) << 32)) return RD_EUNSUPPORTED;
+  st = check_groups(num_groups, group_offset, num_local);
+  if (st != RD_OK) return st;
+  if (out_dtype != RD_BF16 && out_dtype != RD_F32) return RD_EINVAL;
+  if (!w || !group_sizes) return RD_EINVAL;
+  if (m == 0) return RD_OK;  // no rows: x and out may be empty (null)
+  if (!x || !out) return RD_EINVAL;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(out)) return RD_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(group_sizes) & 3u) || (reinterpret_cast<uintptr_t>(limit) & 3u) ||
+      (reinterpret_cast<uintptr_t>(group_offset) & 3u))
+    return RD_EINVAL;
+  rd::GemmProblem p{};
+  p.a = x;
+  p.b = w;
+  p.group_sizes = group_sizes;
+  p.num_groups = num_groups;
+  p.group_offset = group_offset;
+  p.num_local = num_local;
+  p.limit = limit;
+  p.out = out;
+  p.out_f32 = out_dtype == RD_F32;
+  p.m = static_cast<int>(m);
+  p.k = static_cast<int>(k);
+  p.n = static_cast<int>(n);
+  return rd::launch_forward_fp8_trans_rhs(p, static_cast<hipStream_t>(stream));
+}
+
 size_t rd_trans_workspace_size(int64_t m, int64_t k, int64_t n, int32_t num_local) {
   (void)m;
   (void)k;

@@ -39,7 +39,7 @@
 namespace rd {
 namespace {
 
-enum Mode { kFwdNN = 0, kFwdNT = 1, kTransTN = 2 };
+enum Mode { kFwdNN = 0, kFwdNT = 1, kTransTN = 2, kFwdNT8 = 3 };
 
 constexpr int BK = 64;  // contraction elements per pipeline stage
 constexpr int kZeroRows = 16;
@@ -56,6 +56,9 @@ struct KArgs {
 };
 
 #define RD_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------- LDS layouts
 
@@ -82,6 +85,16 @@ struct KLayoutT {
   __device__ __forceinline__ static bf16x8_t frag(const uint16_t* tile, int r_base, int ks) {
     const int l = threadIdx.x & 63;
     return *reinterpret_cast<const bf16x8_t*>(tile + offset(r_base + (l & 31), 2 * ks + (l >> 5)));
+  }
+  // fp8 operand (two fp8 per 16-bit element): lane l gets row (r_base + l %
+  // 32), fp8 contraction elements 64*kk + 32*(l/32) .. +31, i.e. 16-byte
+  // chunks 4*kk + 2*(l/32) and the next one.
+  __device__ __forceinline__ static i32x8_t frag8(const uint16_t* tile, int r_base, int kk) {
+    const int l = threadIdx.x & 63;
+    const int r = r_base + (l & 31), c = 4 * kk + 2 * (l >> 5);
+    const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(tile + offset(r, c));
+    const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(tile + offset(r, c + 1));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
 };
 using KLayout = KLayoutT<BK>;
@@ -753,6 +766,49 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_regs(KArgs p) {
 
 // ---------------------------------------------------------------- streamed buffer-to-LDS kernel
 
+// fp8 K-contiguous operand: the bf16 machinery moves it as pairs of bytes
+// (KS 16-bit elements = 2 * KS fp8 per stage row), only the fragment differs.
+template <int ROWS, int KS>
+struct K8Dma : KDma<ROWS, KS> {
+  __device__ __forceinline__ static i32x8_t frag8(const uint16_t* tile, int r_base, int kk) {
+    return KLayoutT<KS>::frag8(tile, r_base, kk);
+  }
+};
+
+// MFMAs of one stage of fp8 operands: 2 * KS fp8 contraction elements, i.e.
+// KS / 32 slices of the 32x32x64 fp8 MFMA (fp32 accumulation; operand
+// format fields select OCP E4M3 for both operands, no block scaling).
+// Fragments are double-buffered across the slices.
+template <class OpA, class OpB, int MI, int NI, int KS>
+__device__ __forceinline__ void mma_stage8(const uint16_t* ta, const uint16_t* tb, f32x16_t (&acc)[MI][NI],
+                                           int wm_off, int wn_off) {
+  constexpr int kSlices = KS / 32;
+  i32x8_t af[2][MI], bfr[2][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) af[0][mi] = OpA::frag8(ta, wm_off + mi * 32, 0);
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) bfr[0][ni] = OpB::frag8(tb, wn_off + ni * 32, 0);
+#pragma unroll
+  for (int kk = 0; kk < kSlices; ++kk) {
+    const int cur = kk & 1;
+    if (kk + 1 < kSlices) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) af[cur ^ 1][mi] = OpA::frag8(ta, wm_off + mi * 32, kk + 1);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) bfr[cur ^ 1][ni] = OpB::frag8(tb, wn_off + ni * 32, kk + 1);
+    }
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[cur][mi], bfr[cur][ni], acc[mi][ni], 0, 0,
+                                                                      0, 0, 0, 0);
+    if (kk + 1 < kSlices) __builtin_amdgcn_sched_group_barrier(0x100, 2 * (MI + NI), 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, MI * NI, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // Operands of one tile, per mode.
 template <int MODE, int BM, int BN, int KS>
 struct StreamOps;
@@ -773,6 +829,16 @@ struct StreamOps<kFwdNT, BM, BN, KS> {
     a.init(p.a + static_cast<long long>(t.row0) * p.k, t.row_end - t.row0, p.k, wave);
     b.init(p.b + static_cast<long long>(t.j) * p.k * p.n + static_cast<long long>(t.n0) * p.k, p.n - t.n0, p.k,
            wave);
+  }
+};
+// fp8 trans_rhs: x [m, k] and w [g, n, k] as fp8; the kernel sees k / 2
+// 16-bit elements per row (KArgs::k), so the bf16 addressing applies as is.
+template <int BM, int BN, int KS>
+struct StreamOps<kFwdNT8, BM, BN, KS> {
+  using A = K8Dma<BM, KS>;
+  using B = K8Dma<BN, KS>;
+  __device__ __forceinline__ static void make(const KArgs& p, const FwdTiles::Tile& t, int wave, A& a, B& b) {
+    StreamOps<kFwdNT, BM, BN, KS>::make(p, t, wave, a, b);
   }
 };
 template <int BM, int BN, int KS>
@@ -901,12 +967,18 @@ __global__ __launch_bounds__(kThreads, WGS) void grouped_gemm_stream(KArgs p) {
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       const uint16_t* slot = s_tiles + (g % S) * ST;
-      StageFrags<OpA, OpB, MI, NI> fr;
-      stage_frags(slot, slot + A_EL, fr, wm_off, wn_off);
-      __builtin_amdgcn_sched_barrier(0);
-      produce();
-      __builtin_amdgcn_sched_barrier(0);
-      mma_stage<OpA, OpB, MI, NI, KS>(slot, slot + A_EL, fr, acc, wm_off, wn_off);
+      if constexpr (MODE == kFwdNT8) {
+        produce();
+        __builtin_amdgcn_sched_barrier(0);
+        mma_stage8<OpA, OpB, MI, NI, KS>(slot, slot + A_EL, acc, wm_off, wn_off);
+      } else {
+        StageFrags<OpA, OpB, MI, NI> fr;
+        stage_frags(slot, slot + A_EL, fr, wm_off, wn_off);
+        __builtin_amdgcn_sched_barrier(0);
+        produce();
+        __builtin_amdgcn_sched_barrier(0);
+        mma_stage<OpA, OpB, MI, NI, KS>(slot, slot + A_EL, fr, acc, wm_off, wn_off);
+      }
       ++g;
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -1322,6 +1394,17 @@ int launch_forward(const GemmProblem& p, bool trans_rhs, void* workspace, size_t
     else
       launch_one<kFwdNN, 128, 128, 0>(a, work, stream);
   }
+  return hipGetLastError() == hipSuccess ? RD_OK : RD_EHIP;
+}
+
+int launch_forward_fp8_trans_rhs(const GemmProblem& p, hipStream_t stream) {
+  // the kernel addresses fp8 rows as k / 2 16-bit elements
+  GemmProblem q = p;
+  q.k = p.k / 2;
+  const KArgs a = make_args(q);
+  const long long work = (static_cast<long long>((p.m + 127) / 128) + p.num_local) * ((p.n + 255) / 256) +
+                         (p.m + kZeroRows - 1) / kZeroRows + 2;
+  launch_one<kFwdNT8, 128, 256, 3, 64>(a, work, stream);
   return hipGetLastError() == hipSuccess ? RD_OK : RD_EHIP;
 }
 

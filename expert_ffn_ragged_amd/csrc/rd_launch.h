@@ -35,6 +35,8 @@ DecodePlan plan_decode(const GemmProblem& p, bool trans_rhs);
 int launch_forward(const GemmProblem& p, bool trans_rhs, void* workspace, size_t workspace_bytes,
                    hipStream_t stream);
 int launch_trans(const GemmProblem& p, hipStream_t stream);
+// fp8 (OCP E4M3) x [m, k] and w [g, n, k]; requires k % 128 == 0 and k * max(m, n) < 2^32.
+int launch_forward_fp8_trans_rhs(const GemmProblem& p, hipStream_t stream);
 int launch_glu_fwd(const void* fused, const int32_t* limit, void* out, int rows, int h, hipStream_t stream);
 int launch_glu_bwd(const void* fused, const void* d_out, const int32_t* limit, void* d_fused, int rows, int h,
                    hipStream_t stream);

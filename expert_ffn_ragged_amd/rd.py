@@ -29,6 +29,7 @@ EXPORTS = (
     "rd_forward_workspace_size",
     "rd_forward",
     "rd_forward_trans_rhs",
+    "rd_forward_trans_rhs_fp8",
     "rd_trans_workspace_size",
     "rd_trans",
     "rd_glu_fwd",
@@ -63,6 +64,8 @@ def library():
     for name in ("rd_forward", "rd_forward_trans_rhs"):
         getattr(lib, name).restype = ctypes.c_int
         getattr(lib, name).argtypes = fwd
+    lib.rd_forward_trans_rhs_fp8.restype = ctypes.c_int
+    lib.rd_forward_trans_rhs_fp8.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, i32, i64, i64, i64, vp]
     lib.rd_trans_workspace_size.restype = sz
     lib.rd_trans_workspace_size.argtypes = [i64, i64, i64, i32]
     lib.rd_trans.restype = ctypes.c_int
@@ -154,6 +157,32 @@ def ragged_dot(x, w, group_sizes, group_offset=None, limit=None, trans_rhs=False
     _check(fn(_ptr(x), _ptr(w), _ptr(group_sizes), group_sizes.numel(), _ptr(group_offset), gl,
               _ptr(limit), _ptr(out), _DTYPES[out.dtype], m, k, n,
               _ptr(workspace) if ws_bytes else None, ws_bytes, _stream(stream)))
+    return out
+
+
+def ragged_dot_fp8(x, w, group_sizes, group_offset=None, limit=None, out_dtype=torch.bfloat16, out=None,
+                   stream=None):
+    """fp8 (E4M3) ragged_dot in the trans_rhs form: out[rows of local group j] = x[rows] @ w[j].T.
+
+    x: [m, k] torch.float8_e4m3fn; w: [num_local, n, k] torch.float8_e4m3fn; float32 accumulation.
+    """
+    _need(x, "x", torch.float8_e4m3fn, 2)
+    _need(w, "w", torch.float8_e4m3fn, 3)
+    _need(group_sizes, "group_sizes", torch.int32, 1)
+    group_offset = _scalar(group_offset, "group_offset")
+    limit = _scalar(limit, "limit")
+    m, k = x.shape
+    gl, n, kw = w.shape
+    if kw != k:
+        raise ValueError("contraction sizes of x and w differ")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    _need(out, "out", out.dtype, 2)
+    if tuple(out.shape) != (m, n) or out.dtype not in _DTYPES:
+        raise ValueError("out must be [m, n] bf16 or float32")
+    _check(library().rd_forward_trans_rhs_fp8(_ptr(x), _ptr(w), _ptr(group_sizes), group_sizes.numel(),
+                                              _ptr(group_offset), gl, _ptr(limit), _ptr(out), _DTYPES[out.dtype],
+                                              m, k, n, _stream(stream)))
     return out
 
 

@@ -132,6 +132,21 @@ int rd_forward_trans_rhs(const void* x, const void* w, const int32_t* group_size
                          int64_t n, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ragged_dot with trans_rhs on fp8 operands ([SkyRL]: the kernels take a
+ * compute_dtype; the pages report nothing for fp8, so this is the plainest
+ * form): x [m, k] and w [num_local, n, k] hold OCP FP8 E4M3 values (1 sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits; no infinities, S.1111.111 is
+ * NaN), out[r,:] = x[r,:] @ w[j]^T with float32 accumulation of the exact
+ * products, then one rounding to out_dtype.  No scaling factors are applied
+ * (fold them into the inputs or the output).  Window, limit and row rules
+ * are those of rd_forward.  Requires k a multiple of 128 and
+ * k * max(m, n) < 2^32 (else RD_EUNSUPPORTED).
+ */
+int rd_forward_trans_rhs_fp8(const void* x, const void* w, const int32_t* group_sizes, int32_t num_groups,
+                             const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* out,
+                             int32_t out_dtype, int64_t m, int64_t k, int64_t n, void* stream);
+
+/*
  * trans_ragged_dot ([SkyRL], _gpu_trans_ragged_dot_fwd; the weight
  * gradient): dw[j] = x_j^T @ dy_j over the rows of local group j.
  *

@@ -1,0 +1,84 @@
+"""GPU parity of the fp8 (E4M3) trans_rhs ragged_dot against the oracle.
+
+The oracle accumulates the exact products in float64; the kernel in
+float32 through the fp8 MFMA, so the GEMM tolerance applies.  Every E4M3
+value is exactly a bf16 value, so the bf16 kernel on the widened inputs is
+a second, independent reference (same tolerance).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from expert_ffn_ragged_amd import rd, workloads
+from tests.gpu_util import (assert_bf16_is_rne_of_f32, assert_gemm_close, is_pos_zero, is_sentinel, say,
+                            sentinel)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def dev_i32(v):
+    return torch.tensor([int(v)], dtype=torch.int32, device=DEV)
+
+
+def fp8_normal(shape, std, seed):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    return (torch.randn(shape, generator=g, device=DEV) * std).to(torch.float8_e4m3fn)
+
+
+def codes(t):
+    return t.detach().cpu().contiguous().view(torch.uint8).numpy()
+
+
+@pytest.mark.parametrize("off,limit", [(None, None), (1, None), (None, 300), (2, 250)])
+def test_fp8_trans_rhs_small(off, limit):
+    say(f"fp8 trans_rhs off={off} limit={limit}")
+    gs_host = np.array([70, 0, 150, 5, 129, 0, 30], dtype=np.int32)
+    m, k, n = int(gs_host.sum()) + 9, 384, 320
+    gl = 7 if off is None else 4
+    x = fp8_normal((m, k), 1.0, 11)
+    w = fp8_normal((gl, n, k), 0.5, 12)
+    gs = torch.from_numpy(gs_host).to(DEV)
+    offt = None if off is None else dev_i32(off)
+    limt = None if limit is None else dev_i32(limit)
+    o32 = sentinel((m, n), torch.float32)
+    o16 = sentinel((m, n), torch.bfloat16)
+    rd.ragged_dot_fp8(x, w, gs, offt, limt, out=o32)
+    rd.ragged_dot_fp8(x, w, gs, offt, limt, out=o16)
+    # the bf16 kernel on the same (widened) values
+    ob = rd.ragged_dot(x.to(torch.bfloat16), w.to(torch.bfloat16), gs, offt, limt, trans_rhs=True,
+                       out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    lb, lo, hi, L = oracle.boundaries(gs_host, m, off, gl, limit)
+    ref = oracle.ragged_dot_fp8(codes(x), codes(w), gs_host, off, limit)
+    assert_gemm_close(o32[:L].cpu().numpy(), ref, "fp8")
+    assert_gemm_close(ob[:L].cpu().numpy(), ref, "bf16 of fp8 values")
+    outside = torch.ones(L, dtype=torch.bool, device=DEV)
+    outside[lo:hi] = False
+    assert bool(is_pos_zero(o32[:L][outside]).all())
+    assert bool(is_sentinel(o32[L:]).all()) and bool(is_sentinel(o16[L:]).all())
+    assert_bf16_is_rne_of_f32(o16[:L], o32[:L], "fp8")
+
+
+def test_fp8_moe_backward_shape_sampled():
+    """dx of the backward workload (m32768, w[64, 1024, 4096]) with fp8 operands, sampled rows."""
+    say("fp8 trans_rhs backward shape")
+    d = workloads.make(3, DEV, parts=())
+    gs_host = d["gs_host"]
+    m, n, k = 32768, 1024, 4096
+    x = fp8_normal((m, k), 1.0, 21)
+    w = fp8_normal((64, n, k), 0.05, 22)
+    o32 = rd.ragged_dot_fp8(x, w, d["gs"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([rng.integers(0, m, size=96), [0, m - 1]]))
+    lb = np.concatenate([[0], np.cumsum(gs_host)])
+    owner = np.searchsorted(lb, rows, side="right") - 1
+    counts = np.bincount(owner, minlength=64).astype(np.int32)
+    xs = codes(x[torch.from_numpy(rows).to(DEV)])
+    ref = oracle.ragged_dot_fp8(xs, codes(w), counts)
+    assert_gemm_close(o32[torch.from_numpy(rows).to(DEV)].cpu().numpy(), ref, "fp8 backward shape")
