@@ -11,7 +11,7 @@
 
 namespace rd {
 
-constexpr int kThreads = 256;  // every kernel runs 4 wave64s per workgroup
+constexpr int kThreads = 256;  // default workgroup: 4 wave64s (the wide GEMM tiles run 8)
 constexpr int kXcds = 8;       // MI355X: workgroups are dealt round-robin over 8 XCDs
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -41,8 +41,9 @@ __device__ __forceinline__ long long wave_incl_scan(long long x) {
   return x;
 }
 
-// Exclusive scan of one int64 per thread across the 256-thread block.
-// s_wave: 4 int64 of LDS.  Contains two barriers; call from uniform control flow.
+// Exclusive scan of one int64 per thread across the NT-thread block.
+// s_wave: NT / 64 int64 of LDS.  Contains two barriers; call from uniform control flow.
+template <int NT = kThreads>
 __device__ __forceinline__ long long block_excl_scan(long long tot, long long* s_wave) {
   const long long inc = wave_incl_scan(tot);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -64,7 +65,8 @@ struct Window {
 // s_lb[j] = b[off + j] for j in [0, gl].  A window that does not fit
 // (off < 0 or off + gl > G) gives s_lb = 0 everywhere (no rows).
 // L = clamp(*limit, 0, m), or m without a limit.
-// Requires G, gl <= 4 * kThreads.  Ends with a barrier.
+// Requires G, gl <= 4 * NT (NT threads in the block).  Ends with a barrier.
+template <int NT = kThreads>
 __device__ __forceinline__ Window build_local_bounds(const int32_t* __restrict__ gs, int G,
                                                      const int32_t* __restrict__ offp, int gl,
                                                      const int32_t* __restrict__ limp, int m, int* s_lb,
@@ -86,7 +88,7 @@ __device__ __forceinline__ Window build_local_bounds(const int32_t* __restrict__
     v[i] = s > 0 ? s : 0;
     tot += v[i];
   }
-  long long run = block_excl_scan(tot, s_wave);
+  long long run = block_excl_scan<NT>(tot, s_wave);
   if (ok) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -94,19 +96,20 @@ __device__ __forceinline__ Window build_local_bounds(const int32_t* __restrict__
       if (pos >= 0 && pos <= gl) s_lb[pos] = static_cast<int>(run < L ? run : L);
       run += v[i];
     }
-    if (t == kThreads - 1) {  // boundary G when G == 4 * kThreads
-      const int pos = 4 * kThreads - off;
+    if (t == NT - 1) {  // boundary G when G == 4 * NT
+      const int pos = 4 * NT - off;
       if (pos >= 0 && pos <= gl) s_lb[pos] = static_cast<int>(run < L ? run : L);
     }
   } else {
-    for (int j = t; j <= gl; j += kThreads) s_lb[j] = 0;
+    for (int j = t; j <= gl; j += NT) s_lb[j] = 0;
   }
   __syncthreads();
   return Window{s_lb[0], s_lb[gl], L};
 }
 
 // s_out[j] = sum_{i<j} cnt(i) for j in [0, n], cnt(i) = ceil((s_lb[i+1]-s_lb[i]) / tile).
-// Returns the total.  Requires n <= 4 * kThreads.  Ends with a barrier.
+// Returns the total.  Requires n <= 4 * NT.  Ends with a barrier.
+template <int NT = kThreads>
 __device__ __forceinline__ int tile_prefix(const int* s_lb, int n, int tile, int* s_out, long long* s_wave) {
   const int t = threadIdx.x;
   int c[4];
@@ -117,14 +120,14 @@ __device__ __forceinline__ int tile_prefix(const int* s_lb, int n, int tile, int
     c[i] = j < n ? (s_lb[j + 1] - s_lb[j] + tile - 1) / tile : 0;
     tot += c[i];
   }
-  long long run = block_excl_scan(tot, s_wave);
+  long long run = block_excl_scan<NT>(tot, s_wave);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int j = 4 * t + i;
     if (j <= n) s_out[j] = static_cast<int>(run);
     run += c[i];
   }
-  if (t == kThreads - 1 && n == 4 * kThreads) s_out[n] = static_cast<int>(run);
+  if (t == NT - 1 && n == 4 * NT) s_out[n] = static_cast<int>(run);
   __syncthreads();
   return s_out[n];
 }

@@ -10,12 +10,14 @@
 // group_sizes stalls the GPU and breaks graph capture).
 //
 // Design (MI355X):
-//  * one persistent grid of 256-thread workgroups (4 wave64s in a 2x2 layout);
-//    every workgroup scans group_sizes into LDS and walks the tile list;
-//  * bf16 MFMA 32x32x16 with fp32 accumulation over 64-wide K steps;
-//  * main pipeline: A/B tiles go straight from HBM into a 4-stage LDS ring
-//    with 16-byte buffer-to-LDS loads (no VGPR staging), three stages in
-//    flight behind the one being multiplied; per-tile buffer descriptors
+//  * one persistent grid of workgroups of 4 wave64s (2x2 layout; one or two
+//    workgroups per CU) or 8 wave64s (2x4 or 4x2; two waves per SIMD, so a
+//    wave's MFMAs issue while its SIMD partner waits on a barrier or an LDS
+//    read); every workgroup scans group_sizes into LDS and walks the tile list;
+//  * bf16 MFMA 32x32x16 with fp32 accumulation over 32- or 64-wide K steps;
+//  * main pipeline: A/B tiles go straight from HBM into a 2- to 8-slot LDS
+//    ring with 16-byte buffer-to-LDS loads (no VGPR staging), every slot but
+//    one in flight behind the one being multiplied; per-tile buffer descriptors
 //    bound every operand to its valid rows, and the hardware returns zeros
 //    past that bound, so group edges and the packed-buffer limit cost no
 //    instructions and rows >= limit are never fetched;
@@ -268,12 +270,12 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 // wave fills 1 KB slices (64 / (KS/8) rows) of the KLayoutT<KS> tile: lane i
 // writes slot i % (KS/8) of its row, so it fetches the logical chunk stored
 // there (the slot map is an involution).
-template <int ROWS, int KS>
+template <int ROWS, int KS, int NW = 4>
 struct KDma {
   static constexpr int kFragReads = 1;  // LDS reads per MFMA fragment
   static constexpr int kCh = KS / 8;
   static constexpr int kRowsPerSlice = 64 / kCh;
-  static constexpr int kInstr = ROWS / kRowsPerSlice / 4;  // 1 KB slices per wave per stage
+  static constexpr int kInstr = ROWS / kRowsPerSlice / NW;  // 1 KB slices per wave per stage (NW waves)
   static_assert(kInstr >= 1, "tile too small");
   u32x4_t rsrc;
   uint32_t voff[kInstr];
@@ -305,12 +307,12 @@ struct KDma {
 // [mn0, mn0 + COLS).  A 1 KB slice is 512 / COLS rows of the MNLayout tile;
 // lane i writes slot i % (COLS/8) of its row and fetches logical chunk
 // slot ^ swz(row).
-template <int COLS, int KS>
+template <int COLS, int KS, int NW = 4>
 struct MNDma {
   static constexpr int kFragReads = 2;  // LDS reads per MFMA fragment (two transposed 64-bit reads)
   static constexpr int kCpr = COLS / 8;
   static constexpr int kRowsPerSlice = 512 / COLS;
-  static constexpr int kInstr = KS * COLS / 2048;
+  static constexpr int kInstr = KS * COLS / (512 * NW);  // 1 KB slices per wave per stage (NW waves)
   static_assert(kInstr >= 1, "tile too small");
   u32x4_t rsrc;
   uint32_t voff[kInstr];
@@ -488,12 +490,12 @@ constexpr int kStageFloats = 16 * kStagePitch;  // per wave
 // paid once per NI blocks.  No accumulator is copied into general registers
 // wholesale, which keeps 256-accumulator tiles unspilled.  LDS operations of
 // one wave run in order, so the areas are reused safely.
-// Largest divisor of NI whose staging areas (4 waves x NB x kStageFloats
+// Largest divisor of NI whose staging areas (NW waves x NB x kStageFloats
 // floats) fit in `elems` bf16 elements of LDS.
-constexpr int epilogue_batch(int NI, int elems) {
+constexpr int epilogue_batch(int NI, int elems, int NW) {
   int best = 0;
   for (int nb = 1; nb <= NI; ++nb)
-    if (NI % nb == 0 && 4 * nb * kStageFloats * 2 <= elems) best = nb;
+    if (NI % nb == 0 && NW * nb * kStageFloats * 2 <= elems) best = nb;
   return best;
 }
 
@@ -655,9 +657,10 @@ struct TransTiles {
 };
 
 // Groups of the window, largest first (stable), into s_order; plain order
-// when there are more than kThreads local groups.  Ends with a barrier.
+// when there are more than NT local groups (NT threads).  Ends with a barrier.
+template <int NT = kThreads>
 __device__ __forceinline__ void order_groups(const int* s_lb, int gl, int* s_order) {
-  if (gl <= kThreads) {
+  if (gl <= NT) {
     const int t = threadIdx.x;
     if (t < gl) {
       const int sz = s_lb[t + 1] - s_lb[t];
@@ -669,13 +672,14 @@ __device__ __forceinline__ void order_groups(const int* s_lb, int gl, int* s_ord
       s_order[rank] = t;
     }
   } else {
-    for (int t = threadIdx.x; t < gl; t += kThreads) s_order[t] = t;
+    for (int t = threadIdx.x; t < gl; t += NT) s_order[t] = t;
   }
   __syncthreads();
 }
 
 // Rows below L outside the window are written as +0 (rows >= L untouched),
-// in tasks of kZeroRows rows shared by the whole grid.
+// in tasks of kZeroRows rows shared by the whole grid (NT threads per workgroup).
+template <int NT = kThreads>
 __device__ __forceinline__ void zero_outside_window(const KArgs& p, const Window& win) {
   const int z1 = (win.lo + kZeroRows - 1) / kZeroRows;
   const int z2 = (win.L - win.hi + kZeroRows - 1) / kZeroRows;
@@ -692,7 +696,7 @@ __device__ __forceinline__ void zero_outside_window(const KArgs& p, const Window
     }
     uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(p.out) + static_cast<long long>(r0) * p.n * esz);
     const int nch = (r1 - r0) * cpr;
-    for (int q = threadIdx.x; q < nch; q += kThreads) dst[q] = make_uint4(0, 0, 0, 0);
+    for (int q = threadIdx.x; q < nch; q += NT) dst[q] = make_uint4(0, 0, 0, 0);
   }
 }
 
@@ -768,8 +772,8 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_regs(KArgs p) {
 
 // fp8 K-contiguous operand: the bf16 machinery moves it as pairs of bytes
 // (KS 16-bit elements = 2 * KS fp8 per stage row), only the fragment differs.
-template <int ROWS, int KS>
-struct K8Dma : KDma<ROWS, KS> {
+template <int ROWS, int KS, int NW = 4>
+struct K8Dma : KDma<ROWS, KS, NW> {
   __device__ __forceinline__ static i32x8_t frag8(const uint16_t* tile, int r_base, int kk) {
     return KLayoutT<KS>::frag8(tile, r_base, kk);
   }
@@ -809,22 +813,22 @@ __device__ __forceinline__ void mma_stage8(const uint16_t* ta, const uint16_t* t
   }
 }
 
-// Operands of one tile, per mode.
-template <int MODE, int BM, int BN, int KS>
+// Operands of one tile, per mode, loaded by NW waves.
+template <int MODE, int BM, int BN, int KS, int NW>
 struct StreamOps;
-template <int BM, int BN, int KS>
-struct StreamOps<kFwdNN, BM, BN, KS> {
-  using A = KDma<BM, KS>;
-  using B = MNDma<BN, KS>;
+template <int BM, int BN, int KS, int NW>
+struct StreamOps<kFwdNN, BM, BN, KS, NW> {
+  using A = KDma<BM, KS, NW>;
+  using B = MNDma<BN, KS, NW>;
   __device__ __forceinline__ static void make(const KArgs& p, const FwdTiles::Tile& t, int wave, A& a, B& b) {
     a.init(p.a + static_cast<long long>(t.row0) * p.k, t.row_end - t.row0, p.k, wave);
     b.init(p.b + static_cast<long long>(t.j) * p.k * p.n, p.k, p.n, t.n0, wave);
   }
 };
-template <int BM, int BN, int KS>
-struct StreamOps<kFwdNT, BM, BN, KS> {
-  using A = KDma<BM, KS>;
-  using B = KDma<BN, KS>;
+template <int BM, int BN, int KS, int NW>
+struct StreamOps<kFwdNT, BM, BN, KS, NW> {
+  using A = KDma<BM, KS, NW>;
+  using B = KDma<BN, KS, NW>;
   __device__ __forceinline__ static void make(const KArgs& p, const FwdTiles::Tile& t, int wave, A& a, B& b) {
     a.init(p.a + static_cast<long long>(t.row0) * p.k, t.row_end - t.row0, p.k, wave);
     b.init(p.b + static_cast<long long>(t.j) * p.k * p.n + static_cast<long long>(t.n0) * p.k, p.n - t.n0, p.k,
@@ -833,18 +837,18 @@ struct StreamOps<kFwdNT, BM, BN, KS> {
 };
 // fp8 trans_rhs: x [m, k] and w [g, n, k] as fp8; the kernel sees k / 2
 // 16-bit elements per row (KArgs::k), so the bf16 addressing applies as is.
-template <int BM, int BN, int KS>
-struct StreamOps<kFwdNT8, BM, BN, KS> {
-  using A = K8Dma<BM, KS>;
-  using B = K8Dma<BN, KS>;
+template <int BM, int BN, int KS, int NW>
+struct StreamOps<kFwdNT8, BM, BN, KS, NW> {
+  using A = K8Dma<BM, KS, NW>;
+  using B = K8Dma<BN, KS, NW>;
   __device__ __forceinline__ static void make(const KArgs& p, const FwdTiles::Tile& t, int wave, A& a, B& b) {
-    StreamOps<kFwdNT, BM, BN, KS>::make(p, t, wave, a, b);
+    StreamOps<kFwdNT, BM, BN, KS, NW>::make(p, t, wave, a, b);
   }
 };
-template <int BM, int BN, int KS>
-struct StreamOps<kTransTN, BM, BN, KS> {
-  using A = MNDma<BM, KS>;
-  using B = MNDma<BN, KS>;
+template <int BM, int BN, int KS, int NW>
+struct StreamOps<kTransTN, BM, BN, KS, NW> {
+  using A = MNDma<BM, KS, NW>;
+  using B = MNDma<BN, KS, NW>;
   __device__ __forceinline__ static void make(const KArgs& p, const TransTiles::Tile& t, int wave, A& a, B& b) {
     a.init(p.a + static_cast<long long>(t.r_begin) * p.k, t.r_end - t.r_begin, p.k, t.a0, wave);
     b.init(p.b + static_cast<long long>(t.r_begin) * p.n, t.r_end - t.r_begin, p.n, t.c0, wave);
@@ -864,15 +868,19 @@ struct StreamOps<kTransTN, BM, BN, KS> {
 // WGS workgroups share a CU (1, or 2 for the small-ring variant).
 // MAXL bounds num_local for the LDS schedule arrays (a smaller bound frees
 // LDS for a deeper ring; the host only picks such a variant when num_local
-// fits).
-template <int MODE, int BM, int BN, int S, int KS, int WGS, int MAXL = RD_MAX_GROUPS>
-__global__ __launch_bounds__(kThreads, WGS) void grouped_gemm_stream(KArgs p) {
-  constexpr int WM = BM / 2, WN = BN / 2;
+// fits).  The workgroup is WR x WC waves (each owns a BM/WR x BN/WC block of
+// the tile): 2 x 2, or 8 waves (two per SIMD, so one wave's MFMAs issue
+// while the other waits on a barrier or an LDS read).
+template <int MODE, int BM, int BN, int S, int KS, int WGS, int MAXL = RD_MAX_GROUPS, int WR = 2, int WC = 2>
+__global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p) {
+  constexpr int NW = WR * WC, NT = NW * 64;
+  constexpr int WM = BM / WR, WN = BN / WC;
   constexpr int MI = WM / 32, NI = WN / 32;
+  static_assert(MI * 32 == WM && NI * 32 == WN, "wave blocks are whole 32 x 32 MFMA blocks");
   constexpr int A_EL = BM * KS, B_EL = BN * KS, ST = A_EL + B_EL;
-  constexpr int EPI = epilogue_batch(NI, ST);
-  static_assert(EPI >= 1 && 4 * EPI * kStageFloats * 2 <= ST, "epilogue staging must fit in one ring slot");
-  using Ops = StreamOps<MODE, BM, BN, KS>;
+  constexpr int EPI = epilogue_batch(NI, ST, NW);
+  static_assert(EPI >= 1 && NW * EPI * kStageFloats * 2 <= ST, "epilogue staging must fit in one ring slot");
+  using Ops = StreamOps<MODE, BM, BN, KS, NW>;
   using OpA = typename Ops::A;
   using OpB = typename Ops::B;
   using Tiles = typename std::conditional<MODE == kTransTN, TransTiles, FwdTiles>::type;
@@ -880,18 +888,18 @@ __global__ __launch_bounds__(kThreads, WGS) void grouped_gemm_stream(KArgs p) {
   __shared__ __attribute__((aligned(1024))) uint16_t s_tiles[S * ST];
   __shared__ int s_lb[MAXL + 1];
   __shared__ int s_aux[MAXL + 1];
-  __shared__ long long s_wave[kThreads / 64];
+  __shared__ long long s_wave[NW];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm_off = (wave >> 1) * WM, wn_off = (wave & 1) * WN;
-  const Window win = build_local_bounds(p.gs, p.G, p.offp, p.gl, p.limp, p.m, s_lb, s_wave);
+  const int wm_off = (wave / WC) * WM, wn_off = (wave % WC) * WN;
+  const Window win = build_local_bounds<NT>(p.gs, p.G, p.offp, p.gl, p.limp, p.m, s_lb, s_wave);
 
   Tiles tl;
   if constexpr (MODE == kTransTN) {
-    order_groups(s_lb, p.gl, s_aux);
+    order_groups<NT>(s_lb, p.gl, s_aux);
     tl.init(p.gl, p.k, p.n, BM, BN);
   } else {
-    const int total_m = tile_prefix(s_lb, p.gl, BM, s_aux, s_wave);
+    const int total_m = tile_prefix<NT>(s_lb, p.gl, BM, s_aux, s_wave);
     tl.init(total_m, p.n, BN, p.k);
   }
   auto tile_at = [&](long long s, typename Tiles::Tile& t) -> bool {
@@ -987,7 +995,7 @@ __global__ __launch_bounds__(kThreads, WGS) void grouped_gemm_stream(KArgs p) {
     float* stage = reinterpret_cast<float*>(s_tiles + ((g + S - 1) % S) * ST) + wave * EPI * kStageFloats;
     store_wave_tile<MI, NI, EPI>(acc, out, p.out_f32, p.n, r0, rlim, c0, p.n, stage);
   }
-  if constexpr (MODE != kTransTN) zero_outside_window(p, win);
+  if constexpr (MODE != kTransTN) zero_outside_window<NT>(p, win);
 }
 
 // ---------------------------------------------------------------- decode: split contraction
@@ -1242,9 +1250,9 @@ int grid_size(long long work_items, int per_cu) {
 // per MFMA, smaller BM wastes fewer MFMA rows on short groups.
 enum Tile { kT64x128 = 0, kT128x128 = 1, kT128x256 = 2, kT256x256 = 3, kT128x128x2 = 4, kT64x64 = 5, kT256x256k32 = 6,
             kT128x256k32 = 7, kT128x256x2 = 8, kT128x128k32x2 = 9, kT128x128x3 = 10, kT256x128x2 = 11,
-            kT128x256s3x2 = 12, kTileCount };
+            kT128x256s3x2 = 12, kW256x256 = 13, kW128x256 = 14, kW256x256k64 = 15, kTileCount };
 
-// RD_FWD_TILE / RD_TRANS_TILE (0..12) force a shape, for tile sweeps.
+// RD_FWD_TILE / RD_TRANS_TILE (0..15) force a shape, for tile sweeps.
 int forced_tile(const char* name) {
   const char* v = getenv(name);
   if (v == nullptr || *v == 0) return -1;
@@ -1255,19 +1263,19 @@ int forced_tile(const char* name) {
 // Forward shape from what the host knows (never the device-resident group
 // sizes): m / num_local bounds the mean rows per local group.  Decode-sized
 // groups take a 64-row tile (when no workspace allows the split-contraction
-// path); otherwise 128 x 256 tiles with two workgroups per CU (one
-// multiplies while the other drains its stores), with a 3-slot ring for long
-// groups; trans_rhs calls take one workgroup per CU with a 3 x 64-deep ring.
-// Chosen from sweeps of every shape on the up-projection, backward,
-// window+limit and decode workloads.
+// path).  Otherwise 128 x 256 tiles: trans_rhs calls and long groups run
+// eight waves sharing a 3 x 64-deep ring (two waves per SIMD); groups of at
+// most 256 rows (mean) run two 4-wave workgroups per CU (one multiplies
+// while the other drains its stores).  Chosen from sweeps of every shape on
+// the up-projection, backward, window+limit and decode workloads.
 int pick_forward_tile(const GemmProblem& p, bool trans_rhs) {
   const int forced = forced_tile("RD_FWD_TILE");
   if (forced >= 0) return forced;
   const long long avg_rows = p.m / (p.num_local > 0 ? p.num_local : 1);
   if (avg_rows <= 48) return kT64x128;
   if (p.n < 256) return kT128x128;
-  if (trans_rhs) return kT128x256;
-  return avg_rows <= 256 ? kT128x256x2 : kT128x256s3x2;
+  if (trans_rhs) return kW128x256;
+  return avg_rows <= 256 ? kT128x256x2 : kW128x256;
 }
 
 // trans_ragged_dot: the contraction runs over a group's rows.  Two
@@ -1279,12 +1287,13 @@ int pick_trans_tile(const GemmProblem& p) {
   return p.k >= 128 && p.n >= 256 ? kT128x256s3x2 : kT128x128x2;
 }
 
-template <int MODE, int BM, int BN, int S, int KS = 32, int WGS = 1, int MAXL = RD_MAX_GROUPS>
+template <int MODE, int BM, int BN, int S, int KS = 32, int WGS = 1, int MAXL = RD_MAX_GROUPS, int WR = 2,
+          int WC = 2>
 void launch_one(const KArgs& a, long long work, hipStream_t stream) {
   if constexpr (S == 0)
     grouped_gemm_regs<MODE, BM, BN><<<grid_size(work, 2), kThreads, 0, stream>>>(a);
   else
-    grouped_gemm_stream<MODE, BM, BN, S, KS, WGS, MAXL><<<grid_size(work, WGS), kThreads, 0, stream>>>(a);
+    grouped_gemm_stream<MODE, BM, BN, S, KS, WGS, MAXL, WR, WC><<<grid_size(work, WGS), WR * WC * 64, 0, stream>>>(a);
 }
 
 template <int MODE>
@@ -1316,6 +1325,11 @@ void launch_tile(int tile, const KArgs& a, const GemmProblem& p, hipStream_t str
       else
         launch_one<MODE, 128, 256, 2, 32, 2>(a, work(128, 256), stream);
       break;
+    // eight waves (two per SIMD) sharing one ring: 4 x 2 waves of 64 x 128,
+    // 2 x 4 waves of 64 x 64, and the 256 x 256 tile with 64-deep stages
+    case kW256x256: launch_one<MODE, 256, 256, 4, 32, 1, RD_MAX_GROUPS, 4, 2>(a, work(256, 256), stream); break;
+    case kW128x256: launch_one<MODE, 128, 256, 3, 64, 1, RD_MAX_GROUPS, 2, 4>(a, work(128, 256), stream); break;
+    case kW256x256k64: launch_one<MODE, 256, 256, 2, 64, 1, RD_MAX_GROUPS, 4, 2>(a, work(256, 256), stream); break;
     default: launch_one<MODE, 128, 128, 4, 64>(a, work(128, 128), stream); break;
   }
 }
