@@ -218,6 +218,7 @@ def extra_all(steps):
     dy8, w8 = d["dy"].to(torch.float8_e4m3fn), d["w"].to(torch.float8_e4m3fn)
     del d, dw, dw32
     torch.cuda.empty_cache()
+    out.update(glu_epilogue(steps))
     _, _, per = timed_ops([("dx_fp8", lambda: rd.ragged_dot_fp8(dy8, w8, gs3, out=dx))], steps, 3)
     out["backward_m32768_dx_fp8"] = {"ms": round(per["dx_fp8"], 4), "TFLOP/s": round(fl / per["dx_fp8"] / 1e9, 1),
                                      "mfma_frac_fp8": round(fl / per["dx_fp8"] / 1e9 / MFMA_FP8_PEAK_TFLOPS, 4)}
@@ -263,6 +264,34 @@ def extra_all(steps):
     torch.cuda.empty_cache()
     out.update(mlp_layer(steps))
     return out
+
+
+def glu_epilogue(steps):
+    """The up-projection forward (m8192 k4096 h1024 g64) with the GLU as the GEMM's epilogue, writing act
+    alone or act and the [gate | up] buffer, against ragged_dot followed by glu_fwd."""
+    import torch
+
+    from expert_ffn_ragged_amd import rd, workloads
+
+    d = workloads.make(2, "cuda", parts=("x", "w"))
+    x, w, gs = d["x"], d["w"], d["gs"]
+    m, k, n = d["m"], d["k"], d["n"]
+    rows = int(d["gs_host"].sum())
+    fused = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    act = torch.empty((m, n // 2), dtype=torch.bfloat16, device="cuda")
+
+    def separate():
+        rd.ragged_dot(x, w, gs, out=fused)
+        rd.glu_fwd(fused, out=act)
+
+    _, _, per = timed_ops([
+        ("separate", separate),
+        ("fused_act_only", lambda: rd.ragged_dot_glu(x, w, gs, act=act)),
+        ("fused_act_and_buffer", lambda: rd.ragged_dot_glu(x, w, gs, act=act, fused=fused)),
+    ], steps, 3)
+    fl = 2.0 * rows * k * n
+    return {f"upproj_fwd_glu_{key}": {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1)}
+            for key, ms in per.items()}
 
 
 def mlp_layer(steps):

@@ -11,7 +11,8 @@ review's fix for trans_ragged_dot:
 
 The MoE MLP (``moe_mlp``) is the expert FFN of the MaxText page (PR #5760,
 "397B v7x trainer: MoE wo FSDP sharding and valid-rows-only MoE kernels"):
-``fused = ragged_dot(x, wi)`` as ``[gate | up]``, ``act = silu(gate) * up``,
+``fused = ragged_dot(x, wi)`` as ``[gate | up]``, ``act = silu(gate) * up``
+(one kernel with the GLU as the GEMM's epilogue where the shapes allow it),
 ``out = ragged_dot(act, wo)``; its backward keeps the fused buffer as the GLU
 residual (``act`` is recomputed from it, as the page's kernel path does) and
 runs every step on the GPU kernels.  All of a layer's kernels read the same
@@ -87,8 +88,13 @@ class MoeMLP(torch.autograd.Function):
     @staticmethod
     def forward(ctx, x, wi, wo, group_sizes, group_offset=None, limit=None, zero_tail=False):
         m = x.shape[0]
-        fused = rd.ragged_dot(x, wi, group_sizes, group_offset, limit)
-        act = rd.glu_fwd(fused, limit)
+        # one kernel (GEMM + GLU epilogue), except for decode-sized groups, whose split-contraction
+        # ragged_dot path streams the weights faster than the fused tile kernel
+        if m > 24 * wi.shape[0] and rd.glu_epilogue_supported(m, x.shape[1], wi.shape[2] // 2):
+            act, fused = rd.ragged_dot_glu(x, wi, group_sizes, group_offset, limit, want_fused=True)
+        else:
+            fused = rd.ragged_dot(x, wi, group_sizes, group_offset, limit)
+            act = rd.glu_fwd(fused, limit)
         out = torch.zeros((m, wo.shape[2]), dtype=x.dtype, device=x.device) if zero_tail else None
         out = rd.ragged_dot(act, wo, group_sizes, group_offset, limit, out=out)
         ctx.save_for_backward(x, wi, wo, group_sizes, group_offset, limit, fused)

@@ -108,6 +108,38 @@ int rd_forward_trans_rhs(const void* x, const void* w, const int32_t* group_size
                         k, n, workspace, workspace_bytes, stream, true);
 }
 
+int rd_forward_glu(const void* x, const void* wi, const int32_t* group_sizes, int32_t num_groups,
+                   const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* act,
+                   void* fused, int64_t m, int64_t k, int64_t h, void* stream) {
+  int st = check_dims(m, k, 2 * h);
+  if (st != RD_OK) return st;
+  st = check_groups(num_groups, group_offset, num_local);
+  if (st != RD_OK) return st;
+  if (!wi || !group_sizes) return RD_EINVAL;
+  if (m == 0) return RD_OK;  // no rows: x, act and fused may be empty (null)
+  if (!x || !act) return RD_EINVAL;
+  if (!aligned16(x) || !aligned16(wi) || !aligned16(act) || (fused && !aligned16(fused))) return RD_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(group_sizes) & 3u) || (reinterpret_cast<uintptr_t>(limit) & 3u) ||
+      (reinterpret_cast<uintptr_t>(group_offset) & 3u))
+    return RD_EINVAL;
+  rd::GemmProblem p{};
+  p.a = x;
+  p.b = wi;
+  p.group_sizes = group_sizes;
+  p.num_groups = num_groups;
+  p.group_offset = group_offset;
+  p.num_local = num_local;
+  p.limit = limit;
+  p.out = act;
+  p.out2 = fused;
+  p.out_f32 = false;
+  p.m = static_cast<int>(m);
+  p.k = static_cast<int>(k);
+  p.n = static_cast<int>(h);
+  if (!rd::fused_glu_supported(p)) return RD_EUNSUPPORTED;
+  return rd::launch_forward_glu(p, static_cast<hipStream_t>(stream));
+}
+
 int rd_forward_trans_rhs_fp8(const void* x, const void* w, const int32_t* group_sizes, int32_t num_groups,
                              const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* out,
                              int32_t out_dtype, int64_t m, int64_t k, int64_t n, void* stream) {

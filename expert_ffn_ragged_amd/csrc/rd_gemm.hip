@@ -36,12 +36,13 @@
 #include <type_traits>
 
 #include "rd_device.h"
+#include "rd_glu_math.h"
 #include "rd_launch.h"
 
 namespace rd {
 namespace {
 
-enum Mode { kFwdNN = 0, kFwdNT = 1, kTransTN = 2, kFwdNT8 = 3 };
+enum Mode { kFwdNN = 0, kFwdNT = 1, kTransTN = 2, kFwdNT8 = 3, kFwdGLU = 4 };
 
 constexpr int BK = 64;  // contraction elements per pipeline stage
 constexpr int kZeroRows = 16;
@@ -53,6 +54,7 @@ struct KArgs {
   const int32_t* offp;
   const int32_t* limp;
   void* out;
+  void* out2;  // kFwdGLU: the [gate | up] buffer [m, 2n] (may be null); out is silu(gate) * up [m, n]
   int G, gl, out_f32;
   int m, k, n;
 };
@@ -348,6 +350,21 @@ struct MNDma {
 // order, so every read has a whole slice of MFMAs to land).  A fence per slice
 // keeps at most two fragment sets live (with 256 accumulators per lane a
 // deeper hoist would spill).
+// Operands whose tile columns are split in two strips (the fused GLU weight).
+template <class T>
+struct SplitCols : std::false_type {};
+
+// Tile column of a wave's B block ni (wn_off: the wave's column offset, NI
+// blocks per wave).  Split-column operands give each wave NI/2 gate blocks and
+// the NI/2 up blocks of the same columns.
+template <class OpB, int NI>
+__device__ __forceinline__ int b_col(int wn_off, int ni) {
+  if constexpr (SplitCols<OpB>::value)
+    return ni < NI / 2 ? wn_off / 2 + ni * 32 : OpB::kHalf + wn_off / 2 + (ni - NI / 2) * 32;
+  else
+    return wn_off + ni * 32;
+}
+
 template <class OpA, class OpB, int MI, int NI>
 struct StageFrags {
   bf16x8_t a[2][MI], b[2][NI];
@@ -359,7 +376,7 @@ __device__ __forceinline__ void stage_frags(const uint16_t* ta, const uint16_t* 
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) f.a[0][mi] = OpA::frag(ta, wm_off + mi * 32, 0);
 #pragma unroll
-  for (int ni = 0; ni < NI; ++ni) f.b[0][ni] = OpB::frag(tb, wn_off + ni * 32, 0);
+  for (int ni = 0; ni < NI; ++ni) f.b[0][ni] = OpB::frag(tb, b_col<OpB, NI>(wn_off, ni), 0);
 }
 
 template <class OpA, class OpB, int MI, int NI, int KS = BK>
@@ -373,7 +390,7 @@ __device__ __forceinline__ void mma_stage(const uint16_t* ta, const uint16_t* tb
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) f.a[cur ^ 1][mi] = OpA::frag(ta, wm_off + mi * 32, ks + 1);
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) f.b[cur ^ 1][ni] = OpB::frag(tb, wn_off + ni * 32, ks + 1);
+      for (int ni = 0; ni < NI; ++ni) f.b[cur ^ 1][ni] = OpB::frag(tb, b_col<OpB, NI>(wn_off, ni), ks + 1);
     }
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
@@ -499,10 +516,11 @@ constexpr int epilogue_batch(int NI, int elems, int NW) {
   return best;
 }
 
-template <int MI, int NI, int NB = NI>
+// Blocks [B0, B0 + NBLK) of the NI are stored, the first at column c0.
+template <int MI, int NI, int NB = NI, int B0 = 0, int NBLK = NI>
 __device__ __forceinline__ void store_wave_tile(const f32x16_t (&acc)[MI][NI], void* out, bool f32, long long ld,
                                                 int r0, int rlim, int c0, int clim, float* stage) {
-  static_assert(NI % NB == 0, "blocks staged together must divide NI");
+  static_assert(NBLK % NB == 0 && B0 + NBLK <= NI, "blocks staged together must divide the stored range");
   const int l = threadIdx.x & 63;
   const int rr = l >> 2, cc = (l & 3) * 8;  // read-back: row rr of the half, columns cc .. cc+7
 #pragma unroll
@@ -510,13 +528,13 @@ __device__ __forceinline__ void store_wave_tile(const f32x16_t (&acc)[MI][NI], v
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int n0 = 0; n0 < NI; n0 += NB) {
+      for (int n0 = 0; n0 < NBLK; n0 += NB) {
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int v = 8 * h; v < 8 * h + 8; ++v)
           stage[b * kStageFloats + (8 * (v >> 2) - 16 * h + 4 * (l >> 5) + (v & 3)) * kStagePitch + (l & 31)] =
-              acc[mi][n0 + b][v];
+              acc[mi][B0 + n0 + b][v];
       const int grow = r0 + mi * 32 + 16 * h + rr;
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
@@ -552,6 +570,33 @@ __device__ __forceinline__ void store_wave_zero(void* out, bool f32, long long l
     if (r < rlim && c < clim)
       *reinterpret_cast<uint4*>(static_cast<char*>(out) + (r * ld + c) * esz) = make_uint4(0, 0, 0, 0);
   }
+}
+
+// Epilogue of the fused up-projection: the wave's first NI/2 blocks are gate
+// columns and the last NI/2 the matching up columns.  Gate and up are rounded
+// to bf16 (what the [gate | up] buffer holds), the GLU takes them in float32
+// and its result is rounded once: bit for bit what the separate GEMM and GLU
+// kernels give.  The [gate | up] buffer itself is written when fused != null.
+template <int MI, int NI, int NB, int NBH>
+__device__ __forceinline__ void store_glu_tile(const f32x16_t (&acc)[MI][NI], void* act, void* fused, int h,
+                                               int r0, int rlim, int c0, float* stage) {
+  constexpr int NH = NI / 2;
+  if (fused != nullptr) {
+    store_wave_tile<MI, NI, NB, 0, NH>(acc, fused, false, 2ll * h, r0, rlim, c0, h, stage);
+    store_wave_tile<MI, NI, NB, NH, NH>(acc, fused, false, 2ll * h, r0, rlim, h + c0, 2 * h, stage);
+  }
+  f32x16_t g[MI][NH];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int b = 0; b < NH; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float gate = bf16_to_f32(f32_to_bf16(acc[mi][b][v]));
+        const float up = bf16_to_f32(f32_to_bf16(acc[mi][NH + b][v]));
+        g[mi][b][v] = glu_f32(gate, up);
+      }
+  store_wave_tile<MI, NH, NBH>(g, act, false, h, r0, rlim, c0, h, stage);
 }
 
 // ---------------------------------------------------------------- tile lists
@@ -680,11 +725,11 @@ __device__ __forceinline__ void order_groups(const int* s_lb, int gl, int* s_ord
 // Rows below L outside the window are written as +0 (rows >= L untouched),
 // in tasks of kZeroRows rows shared by the whole grid (NT threads per workgroup).
 template <int NT = kThreads>
-__device__ __forceinline__ void zero_outside_window(const KArgs& p, const Window& win) {
+__device__ __forceinline__ void zero_outside_window(void* out, int n, bool f32, const Window& win) {
   const int z1 = (win.lo + kZeroRows - 1) / kZeroRows;
   const int z2 = (win.L - win.hi + kZeroRows - 1) / kZeroRows;
-  const int esz = p.out_f32 ? 4 : 2;
-  const int cpr = p.n * esz / 16;
+  const int esz = f32 ? 4 : 2;
+  const int cpr = n * esz / 16;
   for (int z = blockIdx.x; z < z1 + z2; z += gridDim.x) {
     int r0, r1;
     if (z < z1) {
@@ -694,7 +739,7 @@ __device__ __forceinline__ void zero_outside_window(const KArgs& p, const Window
       r0 = win.hi + (z - z1) * kZeroRows;
       r1 = min(r0 + kZeroRows, win.L);
     }
-    uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(p.out) + static_cast<long long>(r0) * p.n * esz);
+    uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(out) + static_cast<long long>(r0) * n * esz);
     const int nch = (r1 - r0) * cpr;
     for (int q = threadIdx.x; q < nch; q += NT) dst[q] = make_uint4(0, 0, 0, 0);
   }
@@ -745,7 +790,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_regs(KArgs p) {
       store_wave_tile<MI, NI>(acc, p.out, p.out_f32, p.n, t.row0 + wm_off, t.row_end, t.n0 + wn_off, p.n, stage);
       __syncthreads();  // staging area = pipeline buffers: drain before the next tile refills them
     }
-    zero_outside_window(p, win);
+    zero_outside_window(p.out, p.n, p.out_f32 != 0, win);
   } else {
     order_groups(s_lb, p.gl, s_aux);
     TransTiles tl;
@@ -778,6 +823,32 @@ struct K8Dma : KDma<ROWS, KS, NW> {
     return KLayoutT<KS>::frag8(tile, r_base, kk);
   }
 };
+
+// Weight operand of the fused up-projection: the tile's BN columns are two
+// strips of w [k, 2h], gate columns [c0, c0 + BN/2) and the matching up
+// columns [h + c0, h + c0 + BN/2), stored as two MN-contiguous sub-tiles.
+template <int BN, int KS, int NW = 4>
+struct GluDma {
+  using Half = MNDma<BN / 2, KS, NW>;
+  static constexpr int kHalf = BN / 2;
+  static constexpr int kFragReads = Half::kFragReads;
+  static constexpr int kInstr = 2 * Half::kInstr;
+  Half g, u;
+  __device__ __forceinline__ void init(const uint16_t* base, long long rows_valid, int ld, int c0, int h, int wave) {
+    g.init(base, rows_valid, ld, c0, wave);
+    u.init(base, rows_valid, ld, h + c0, wave);
+  }
+  __device__ __forceinline__ void issue(uint32_t tile, int kt, int wave) const {
+    g.issue(tile, kt, wave);
+    u.issue(tile + KS * kHalf * 2, kt, wave);
+  }
+  __device__ __forceinline__ static bf16x8_t frag(const uint16_t* tile, int c_base, int ks) {
+    return c_base < kHalf ? MNOperand<kHalf>::frag(tile, c_base, ks)
+                          : MNOperand<kHalf>::frag(tile + KS * kHalf, c_base - kHalf, ks);
+  }
+};
+template <int BN, int KS, int NW>
+struct SplitCols<GluDma<BN, KS, NW>> : std::true_type {};
 
 // MFMAs of one stage of fp8 operands: 2 * KS fp8 contraction elements, i.e.
 // KS / 32 slices of the 32x32x64 fp8 MFMA (fp32 accumulation; operand
@@ -855,6 +926,18 @@ struct StreamOps<kTransTN, BM, BN, KS, NW> {
   }
 };
 
+// Fused up-projection: x [m, k] and w [g, k, 2h]; the tile's gate columns
+// start at t.n0 (KArgs::n is h).
+template <int BM, int BN, int KS, int NW>
+struct StreamOps<kFwdGLU, BM, BN, KS, NW> {
+  using A = KDma<BM, KS, NW>;
+  using B = GluDma<BN, KS, NW>;
+  __device__ __forceinline__ static void make(const KArgs& p, const FwdTiles::Tile& t, int wave, A& a, B& b) {
+    a.init(p.a + static_cast<long long>(t.row0) * p.k, t.row_end - t.row0, p.k, wave);
+    b.init(p.b + static_cast<long long>(t.j) * p.k * 2 * p.n, p.k, 2 * p.n, t.n0, p.n, wave);
+  }
+};
+
 // One persistent stream of contraction steps across all of a workgroup's
 // tiles.  A producer walks the workgroup's tile list issuing buffer-to-LDS
 // loads S-1 steps ahead of the consumer, crossing tile boundaries, so the
@@ -880,6 +963,10 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
   constexpr int A_EL = BM * KS, B_EL = BN * KS, ST = A_EL + B_EL;
   constexpr int EPI = epilogue_batch(NI, ST, NW);
   static_assert(EPI >= 1 && NW * EPI * kStageFloats * 2 <= ST, "epilogue staging must fit in one ring slot");
+  // the fused GLU tile: BN weight columns are BN/2 gate + BN/2 up, giving BN/2 output columns
+  constexpr int TN = MODE == kFwdGLU ? BN / 2 : BN;
+  constexpr int EPI_H = MODE == kFwdGLU ? epilogue_batch(NI / 2, ST, NW) : 1;
+  static_assert(MODE != kFwdGLU || (NI % 2 == 0 && EPI_H >= 1 && EPI_H <= EPI), "GLU tiles pair gate and up blocks");
   using Ops = StreamOps<MODE, BM, BN, KS, NW>;
   using OpA = typename Ops::A;
   using OpB = typename Ops::B;
@@ -900,13 +987,13 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
     tl.init(p.gl, p.k, p.n, BM, BN);
   } else {
     const int total_m = tile_prefix<NT>(s_lb, p.gl, BM, s_aux, s_wave);
-    tl.init(total_m, p.n, BN, p.k);
+    tl.init(total_m, p.n, TN, p.k);
   }
   auto tile_at = [&](long long s, typename Tiles::Tile& t) -> bool {
     if constexpr (MODE == kTransTN)
       return tl.template get<BM, BN, KS>(s, s_lb, s_aux, t);
     else
-      return tl.template get<BM, BN, KS>(s, s_lb, s_aux, p.gl, p.k, t);
+      return tl.template get<BM, TN, KS>(s, s_lb, s_aux, p.gl, p.k, t);
   };
   const uint32_t ring = lds_address(s_tiles);
   const long long stride = gridDim.x;
@@ -958,7 +1045,7 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
       out = static_cast<char*>(p.out);
       r0 = t.row0 + wm_off;
       rlim = t.row_end;
-      c0 = t.n0 + wn_off;
+      c0 = t.n0 + (MODE == kFwdGLU ? wn_off / 2 : wn_off);
     }
     if (t.nk == 0) {  // a local group with no rows: its dW tile is +0
       store_wave_zero<MI, NI>(out, p.out_f32, p.n, r0, rlim, c0, p.n);
@@ -993,9 +1080,14 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
     __builtin_amdgcn_s_barrier();  // every wave is done with the last step's slot
     __builtin_amdgcn_sched_barrier(0);
     float* stage = reinterpret_cast<float*>(s_tiles + ((g + S - 1) % S) * ST) + wave * EPI * kStageFloats;
-    store_wave_tile<MI, NI, EPI>(acc, out, p.out_f32, p.n, r0, rlim, c0, p.n, stage);
+    if constexpr (MODE == kFwdGLU)
+      store_glu_tile<MI, NI, EPI_H, EPI_H>(acc, p.out, p.out2, p.n, r0, rlim, c0, stage);
+    else
+      store_wave_tile<MI, NI, EPI>(acc, out, p.out_f32, p.n, r0, rlim, c0, p.n, stage);
   }
-  if constexpr (MODE != kTransTN) zero_outside_window<NT>(p, win);
+  if constexpr (MODE != kTransTN) zero_outside_window<NT>(p.out, p.n, p.out_f32 != 0, win);
+  if constexpr (MODE == kFwdGLU)
+    if (p.out2 != nullptr) zero_outside_window<NT>(p.out2, 2 * p.n, false, win);
 }
 
 // ---------------------------------------------------------------- decode: split contraction
@@ -1235,6 +1327,7 @@ KArgs make_args(const GemmProblem& p) {
   a.m = p.m;
   a.k = p.k;
   a.n = p.n;
+  a.out2 = p.out2;
   return a;
 }
 
@@ -1250,9 +1343,9 @@ int grid_size(long long work_items, int per_cu) {
 // per MFMA, smaller BM wastes fewer MFMA rows on short groups.
 enum Tile { kT64x128 = 0, kT128x128 = 1, kT128x256 = 2, kT256x256 = 3, kT128x128x2 = 4, kT64x64 = 5, kT256x256k32 = 6,
             kT128x256k32 = 7, kT128x256x2 = 8, kT128x128k32x2 = 9, kT128x128x3 = 10, kT256x128x2 = 11,
-            kT128x256s3x2 = 12, kW256x256 = 13, kW128x256 = 14, kW256x256k64 = 15, kTileCount };
+            kT128x256s3x2 = 12, kW256x256 = 13, kW128x256 = 14, kW256x256k64 = 15, kW128x512 = 16, kTileCount };
 
-// RD_FWD_TILE / RD_TRANS_TILE (0..15) force a shape, for tile sweeps.
+// RD_FWD_TILE / RD_TRANS_TILE (0..16) force a shape, for tile sweeps.
 int forced_tile(const char* name) {
   const char* v = getenv(name);
   if (v == nullptr || *v == 0) return -1;
@@ -1263,11 +1356,14 @@ int forced_tile(const char* name) {
 // Forward shape from what the host knows (never the device-resident group
 // sizes): m / num_local bounds the mean rows per local group.  Decode-sized
 // groups take a 64-row tile (when no workspace allows the split-contraction
-// path).  Otherwise 128 x 256 tiles: trans_rhs calls and long groups run
-// eight waves sharing a 3 x 64-deep ring (two waves per SIMD); groups of at
-// most 256 rows (mean) run two 4-wave workgroups per CU (one multiplies
-// while the other drains its stores).  Chosen from sweeps of every shape on
-// the up-projection, backward, window+limit and decode workloads.
+// path).  trans_rhs calls and long groups take 128 x 256 tiles of eight
+// waves sharing a 3 x 64-deep ring (two waves per SIMD).  Groups of at most
+// 256 rows (mean), where streaming the weights dominates, take 128 x 512
+// tiles of eight waves when n allows (each x row block is read by half as
+// many tiles, each weight row is read 1 KB at a time), else two 4-wave
+// 128 x 256 workgroups per CU (one multiplies while the other drains its
+// stores).  Chosen from sweeps of every shape on the up-projection,
+// backward, window+limit and decode workloads.
 int pick_forward_tile(const GemmProblem& p, bool trans_rhs) {
   const int forced = forced_tile("RD_FWD_TILE");
   if (forced >= 0) return forced;
@@ -1275,7 +1371,8 @@ int pick_forward_tile(const GemmProblem& p, bool trans_rhs) {
   if (avg_rows <= 48) return kT64x128;
   if (p.n < 256) return kT128x128;
   if (trans_rhs) return kW128x256;
-  return avg_rows <= 256 ? kT128x256x2 : kW128x256;
+  if (avg_rows <= 256) return p.n % 512 == 0 ? kW128x512 : kT128x256x2;
+  return kW128x256;
 }
 
 // trans_ragged_dot: the contraction runs over a group's rows.  Two
@@ -1330,6 +1427,7 @@ void launch_tile(int tile, const KArgs& a, const GemmProblem& p, hipStream_t str
     case kW256x256: launch_one<MODE, 256, 256, 4, 32, 1, RD_MAX_GROUPS, 4, 2>(a, work(256, 256), stream); break;
     case kW128x256: launch_one<MODE, 128, 256, 3, 64, 1, RD_MAX_GROUPS, 2, 4>(a, work(128, 256), stream); break;
     case kW256x256k64: launch_one<MODE, 256, 256, 2, 64, 1, RD_MAX_GROUPS, 4, 2>(a, work(256, 256), stream); break;
+    case kW128x512: launch_one<MODE, 128, 512, 3, 32, 1, RD_MAX_GROUPS, 2, 4>(a, work(128, 512), stream); break;
     default: launch_one<MODE, 128, 128, 4, 64>(a, work(128, 128), stream); break;
   }
 }
@@ -1407,6 +1505,37 @@ int launch_forward(const GemmProblem& p, bool trans_rhs, void* workspace, size_t
       launch_one<kFwdNT, 128, 128, 0>(a, work, stream);
     else
       launch_one<kFwdNN, 128, 128, 0>(a, work, stream);
+  }
+  return hipGetLastError() == hipSuccess ? RD_OK : RD_EHIP;
+}
+
+bool fused_glu_supported(const GemmProblem& p) {
+  return p.k % BK == 0 && p.n % 128 == 0 && fits_32bit(p.m, p.k) && fits_32bit(p.k, 2ll * p.n);
+}
+
+// The fused up-projection takes the forward's tile shapes, each weight tile
+// split into gate and up halves (a 512-wide tile gives 256 GLU columns, a
+// 256-wide one 128, the short-group 128-wide one 64).
+int launch_forward_glu(const GemmProblem& p, hipStream_t stream) {
+  if (!fused_glu_supported(p)) return RD_EUNSUPPORTED;
+  const KArgs a = make_args(p);
+  auto work = [&](int BM, int TN) {
+    return (static_cast<long long>((p.m + BM - 1) / BM) + p.num_local) * ((p.n + TN - 1) / TN) +
+           (p.m + kZeroRows - 1) / kZeroRows + 2;
+  };
+  int tile = forced_tile("RD_FWD_TILE");
+  if (tile == kW128x512 && p.n % 256 != 0) tile = -1;  // the 512-column tile needs h % 256 == 0
+  if (tile != kT64x128 && tile != kT128x256 && tile != kT128x256x2 && tile != kW128x256 && tile != kW128x512) {
+    const long long avg_rows = p.m / (p.num_local > 0 ? p.num_local : 1);
+    tile = avg_rows <= 48 ? kT64x128 : avg_rows > 256 ? kW128x256 : p.n % 256 == 0 ? kW128x512 : kT128x256x2;
+  }
+  switch (tile) {
+    case kT64x128: launch_one<kFwdGLU, 64, 128, 6, 64>(a, work(64, 64), stream); break;
+    case kT128x256: launch_one<kFwdGLU, 128, 256, 3, 64>(a, work(128, 128), stream); break;
+    case kT128x256x2: launch_one<kFwdGLU, 128, 256, 2, 32, 2>(a, work(128, 128), stream); break;
+    // 256 gate + 256 up columns per tile (512-byte weight rows), 2 x 4 waves of 64 x 128
+    case kW128x512: launch_one<kFwdGLU, 128, 512, 3, 32, 1, RD_MAX_GROUPS, 2, 4>(a, work(128, 256), stream); break;
+    default: launch_one<kFwdGLU, 128, 256, 3, 64, 1, RD_MAX_GROUPS, 2, 4>(a, work(128, 128), stream); break;
   }
   return hipGetLastError() == hipSuccess ? RD_OK : RD_EHIP;
 }

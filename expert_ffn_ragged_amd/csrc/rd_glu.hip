@@ -24,6 +24,7 @@
 // valid rows, one wave per row, with 128-bit non-temporal loads and stores of
 // 16-byte chunks (8 bf16; the data is touched once).
 #include "rd_device.h"
+#include "rd_glu_math.h"
 #include "rd_launch.h"
 
 #pragma clang fp contract(off)
@@ -37,10 +38,6 @@ __device__ __forceinline__ int clamp_limit(const int32_t* limp, int rows) {
   return v < 0 ? 0 : (v > rows ? rows : v);
 }
 
-constexpr float kLog2e = 1.44269504088896341f;
-constexpr float kTwoM64 = 5.42101086242752217e-20f;  // 2^-64
-constexpr float kTwo64 = 1.8446744073709551616e19f;  // 2^64
-
 typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
 
 // 128-bit loads and stores marked non-temporal (streamed once, not kept in cache).
@@ -53,26 +50,8 @@ __device__ __forceinline__ void nt_store(uint16_t* p, uint4 v) {
   __builtin_nontemporal_store(x, reinterpret_cast<nt_u32x4*>(p));
 }
 
-// den = 1 + exp(-g); x / den as (x * rcp(den * sc)) * sc with sc = 2^-64
-// when den > 2^64 (then g < -44, so x * rcp stays finite) and sc = 1 otherwise.
-struct ScaledRcp {
-  float r, sc;
-};
-__device__ __forceinline__ ScaledRcp rcp_den(float g) {
-  const float den = __builtin_amdgcn_exp2f(-g * kLog2e) + 1.0f;
-  const float sc = den > kTwo64 ? kTwoM64 : 1.0f;
-  return ScaledRcp{__builtin_amdgcn_rcpf(den * sc), sc};
-}
-__device__ __forceinline__ float div_den(float x, const ScaledRcp& q) { return (x * q.r) * q.sc; }
-
 __device__ __forceinline__ float lo16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// silu(g) * u in the page's op order: negate, exp, + 1, divide, multiply.
-__device__ __forceinline__ float glu_f32(float g, float u) {
-  const float s = div_den(g, rcp_den(g));
-  return s * u;
-}
 
 __device__ __forceinline__ uint32_t glu_word(uint32_t gw, uint32_t uw) {
   return pack_bf16x2(glu_f32(lo16(gw), lo16(uw)), glu_f32(hi16(gw), hi16(uw)));

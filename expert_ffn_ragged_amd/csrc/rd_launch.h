@@ -17,9 +17,10 @@ struct GemmProblem {
   const int32_t* group_offset;  // may be null
   int32_t num_local;
   const int32_t* limit;          // may be null
-  void* out;                 // forward: [m,n]; trans: [gl,k,n]
+  void* out;                 // forward: [m,n]; trans: [gl,k,n]; fused GLU: silu(gate) * up [m,n]
   bool out_f32;
-  int m, k, n;
+  int m, k, n;                // fused GLU: n = h, the weight is [gl,k,2h]
+  void* out2 = nullptr;       // fused GLU only: the [gate | up] buffer [m,2h], or null
 };
 
 // Workspace plan of the split-contraction decode path (use == false: the
@@ -37,6 +38,10 @@ int launch_forward(const GemmProblem& p, bool trans_rhs, void* workspace, size_t
 int launch_trans(const GemmProblem& p, hipStream_t stream);
 // fp8 (OCP E4M3) x [m, k] and w [g, n, k]; requires k % 128 == 0 and k * max(m, n) < 2^32.
 int launch_forward_fp8_trans_rhs(const GemmProblem& p, hipStream_t stream);
+// ragged_dot(x, w) with the GLU as its epilogue; requires k % 64 == 0, n (= h) % 128 == 0 and
+// operands under 4 GiB (fused_glu_supported).
+bool fused_glu_supported(const GemmProblem& p);
+int launch_forward_glu(const GemmProblem& p, hipStream_t stream);
 int launch_glu_fwd(const void* fused, const int32_t* limit, void* out, int rows, int h, hipStream_t stream);
 int launch_glu_bwd(const void* fused, const void* d_out, const int32_t* limit, void* d_fused, int rows, int h,
                    hipStream_t stream);

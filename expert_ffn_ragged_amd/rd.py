@@ -18,7 +18,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librd.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 RD_OK, RD_EINVAL, RD_EUNSUPPORTED, RD_EHIP = 0, 1, 2, 3
 RD_BF16, RD_F32 = 0, 1
 _DTYPES = {torch.bfloat16: RD_BF16, torch.float32: RD_F32}
@@ -30,6 +30,7 @@ EXPORTS = (
     "rd_forward",
     "rd_forward_trans_rhs",
     "rd_forward_trans_rhs_fp8",
+    "rd_forward_glu",
     "rd_trans_workspace_size",
     "rd_trans",
     "rd_glu_fwd",
@@ -66,6 +67,7 @@ def library():
         getattr(lib, name).argtypes = fwd
     lib.rd_forward_trans_rhs_fp8.restype = ctypes.c_int
     lib.rd_forward_trans_rhs_fp8.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, i32, i64, i64, i64, vp]
+    lib.rd_forward_glu.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, vp, i64, i64, i64, vp]
     lib.rd_trans_workspace_size.restype = sz
     lib.rd_trans_workspace_size.argtypes = [i64, i64, i64, i32]
     lib.rd_trans.restype = ctypes.c_int
@@ -184,6 +186,45 @@ def ragged_dot_fp8(x, w, group_sizes, group_offset=None, limit=None, out_dtype=t
                                               _ptr(group_offset), gl, _ptr(limit), _ptr(out), _DTYPES[out.dtype],
                                               m, k, n, _stream(stream)))
     return out
+
+
+def glu_epilogue_supported(m, k, h):
+    """Whether ragged_dot_glu takes these sizes: k % 64 == 0, h % 128 == 0, every operand under 4 GiB."""
+    return k % 64 == 0 and h % 128 == 0 and h > 0 and m * k * 2 < 1 << 32 and k * 2 * h * 2 < 1 << 32
+
+
+def ragged_dot_glu(x, wi, group_sizes, group_offset=None, limit=None, act=None, fused=None, want_fused=False,
+                   stream=None):
+    """The up-projection with the GLU as its epilogue: act = glu_fwd(ragged_dot(x, wi)), bit for bit.
+
+    x: [m, k] bf16; wi: [num_local, k, 2h] bf16 ([gate | up] columns).  Returns act [m, h] bf16, or
+    (act, fused) with the [gate | up] buffer fused [m, 2h] when want_fused (or a fused tensor) is given.
+    Requires k % 64 == 0 and h % 128 == 0.
+    """
+    _need(x, "x", torch.bfloat16, 2)
+    _need(wi, "wi", torch.bfloat16, 3)
+    _need(group_sizes, "group_sizes", torch.int32, 1)
+    group_offset = _scalar(group_offset, "group_offset")
+    limit = _scalar(limit, "limit")
+    m, k = x.shape
+    gl, kw, h2 = wi.shape
+    if kw != k or h2 % 2:
+        raise ValueError("wi must be [num_local, k, 2h] with x's k")
+    h = h2 // 2
+    if act is None:
+        act = torch.empty((m, h), dtype=torch.bfloat16, device=x.device)
+    _need(act, "act", torch.bfloat16, 2)
+    if tuple(act.shape) != (m, h):
+        raise ValueError("act must be [m, h]")
+    if fused is None and want_fused:
+        fused = torch.empty((m, h2), dtype=torch.bfloat16, device=x.device)
+    if fused is not None:
+        _need(fused, "fused", torch.bfloat16, 2)
+        if tuple(fused.shape) != (m, h2):
+            raise ValueError("fused must be [m, 2h]")
+    _check(library().rd_forward_glu(_ptr(x), _ptr(wi), _ptr(group_sizes), group_sizes.numel(), _ptr(group_offset),
+                                    gl, _ptr(limit), _ptr(act), _ptr(fused), m, k, h, _stream(stream)))
+    return act if fused is None else (act, fused)
 
 
 def trans_ragged_dot(x, dy, group_sizes, num_local=None, group_offset=None, limit=None,

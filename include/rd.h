@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define RD_ABI_VERSION 2
+#define RD_ABI_VERSION 3
 
 /* status codes */
 #define RD_OK 0
@@ -168,6 +168,37 @@ int rd_trans(const void* x, const void* dy, const int32_t* group_sizes, int32_t 
              const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* dw,
              int32_t dw_dtype, int64_t m, int64_t k, int64_t n, void* workspace,
              size_t workspace_bytes, void* stream);
+
+/*
+ * The MoE up-projection with the GLU as its epilogue ([MaxText]: the expert
+ * FFN computes fused = ragged_dot(x, wi) as [gate | up] and then
+ * silu(gate) * up; [SkyRL] ragged_dot and the group_offset window).  One
+ * kernel computes
+ *
+ *   fused = bf16(ragged_dot(x, wi))           (as rd_forward, out_dtype bf16)
+ *   act   = the rd_glu_fwd result on fused     (same float32 evaluation)
+ *
+ * and is bit-identical to rd_forward without a workspace followed by
+ * rd_glu_fwd: each tile pairs gate columns [c, c + 128) with up columns
+ * [h + c, h + c + 128), rounds both to bf16 as the [gate | up] buffer holds
+ * them, and evaluates the GLU on them.  (rd_forward's split-contraction
+ * decode path, taken only with a workspace, sums in another order.)
+ *
+ *   x     [m, k] bf16.
+ *   wi    [num_local, k, 2h] bf16: columns [0, h) gate, [h, 2h) up.
+ *   act   [m, h] bf16 (output).
+ *   fused [m, 2h] bf16 (output) or NULL: the [gate | up] buffer (the
+ *         backward's residual) is then not written at all.
+ *
+ * group_sizes, group_offset, num_local and limit as rd_forward: rows below L
+ * outside the window are +0 in act (and fused), rows >= L are neither read
+ * nor written.  Requires k a multiple of 64, h a multiple of 128, and every
+ * operand under 4 GiB (else RD_EUNSUPPORTED).  With m == 0 nothing is
+ * launched and x, act, fused may be NULL.
+ */
+int rd_forward_glu(const void* x, const void* wi, const int32_t* group_sizes, int32_t num_groups,
+                   const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* act,
+                   void* fused, int64_t m, int64_t k, int64_t h, void* stream);
 
 /*
  * GLU forward over the valid rows ([MaxText], glu_rows forward).

@@ -46,7 +46,7 @@ def test_links_the_same_hip_runtime_soname_as_torch():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.rd_abi_version() == rd.ABI_VERSION == 2
+    assert lib.rd_abi_version() == rd.ABI_VERSION == 3
     for s in (0, 1, 2, 3, 99):
         assert isinstance(lib.rd_status_string(s), bytes)
     assert lib.rd_trans_workspace_size(100, 64, 64, 4) == 0
@@ -129,3 +129,26 @@ def test_unsort_rejects_bad_arguments(lib):
     assert call(w=18) == rd.RD_EINVAL          # misaligned float
     assert call(limit=18) == rd.RD_EINVAL      # misaligned int32
     assert call(rows=0, g=None, y=None, w=None, grad=None, dot=None) == rd.RD_OK
+
+
+def test_forward_glu_rejects_bad_arguments(lib):
+    """The fused up-projection + GLU: shape rules (k % 64, h % 128) and pointers, checked before launch."""
+    v = ctypes.c_void_p
+    ok = dict(x=16, w=16, gs=16, G=4, off=None, gl=4, limit=None, act=16, fused=None, m=8, k=64, h=128)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        p = lambda x: None if x is None else v(x)
+        return lib.rd_forward_glu(p(a["x"]), p(a["w"]), p(a["gs"]), a["G"], p(a["off"]), a["gl"], p(a["limit"]),
+                                  p(a["act"]), p(a["fused"]), a["m"], a["k"], a["h"], None)
+    assert call(h=64) == rd.RD_EUNSUPPORTED        # h not a multiple of 128
+    assert call(k=72) == rd.RD_EUNSUPPORTED        # k not a multiple of 64
+    assert call(k=12) == rd.RD_EUNSUPPORTED        # k not a multiple of 8
+    assert call(h=0) == rd.RD_EINVAL
+    assert call(act=None) == rd.RD_EINVAL
+    assert call(w=None) == rd.RD_EINVAL
+    assert call(fused=24) == rd.RD_EINVAL          # misaligned
+    assert call(x=40) == rd.RD_EINVAL              # misaligned
+    assert call(gl=5, off=16) == rd.RD_EINVAL      # num_local > num_groups
+    assert call(m=0, x=None, act=None) == rd.RD_OK  # nothing to do, nothing launched
