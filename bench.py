@@ -219,7 +219,7 @@ def extra_all(steps):
     del d, dw, dw32
     torch.cuda.empty_cache()
     out.update(glu_epilogue(steps))
-    _, _, per = timed_ops([("dx_fp8", lambda: rd.ragged_dot_fp8(dy8, w8, gs3, out=dx))], steps, 3)
+    _, _, per = timed_ops([("dx_fp8", lambda: rd.ragged_dot_fp8(dy8, w8, gs3, trans_rhs=True, out=dx))], steps, 3)
     out["backward_m32768_dx_fp8"] = {"ms": round(per["dx_fp8"], 4), "TFLOP/s": round(fl / per["dx_fp8"] / 1e9, 1),
                                      "mfma_frac_fp8": round(fl / per["dx_fp8"] / 1e9 / MFMA_FP8_PEAK_TFLOPS, 4)}
     del dy8, w8, dx
@@ -290,8 +290,17 @@ def glu_epilogue(steps):
         ("fused_act_and_buffer", lambda: rd.ragged_dot_glu(x, w, gs, act=act, fused=fused)),
     ], steps, 3)
     fl = 2.0 * rows * k * n
-    return {f"upproj_fwd_glu_{key}": {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1)}
-            for key, ms in per.items()}
+    out = {f"upproj_fwd_glu_{key}": {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1)}
+           for key, ms in per.items()}
+    # the same forward with fp8 (E4M3) operands, plain form: half the weight bytes
+    x8, w8 = x.to(torch.float8_e4m3fn), w.to(torch.float8_e4m3fn)
+    o = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    _, _, per = timed_ops([("fp8", lambda: rd.ragged_dot_fp8(x8, w8, gs, out=o))], steps, 3)
+    ms = per["fp8"]
+    nb = rows * k + w8.numel() + rows * n * 2
+    out["upproj_fwd_fp8"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1),
+                             "GB/s": round(nb / ms / 1e6, 1), "hbm_frac": round(nb / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    return out
 
 
 def mlp_layer(steps):

@@ -140,12 +140,13 @@ int rd_forward_glu(const void* x, const void* wi, const int32_t* group_sizes, in
   return rd::launch_forward_glu(p, static_cast<hipStream_t>(stream));
 }
 
-int rd_forward_trans_rhs_fp8(const void* x, const void* w, const int32_t* group_sizes, int32_t num_groups,
-                             const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* out,
-                             int32_t out_dtype, int64_t m, int64_t k, int64_t n, void* stream) {
+namespace {
+int forward_fp8(const void* x, const void* w, const int32_t* group_sizes, int32_t num_groups,
+                const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* out, int32_t out_dtype,
+                int64_t m, int64_t k, int64_t n, void* stream, bool trans_rhs) {
   int st = check_dims(m, k, n);
   if (st != RD_OK) return st;
-  if ((k % 128) != 0) return RD_EUNSUPPORTED;
+  if ((k % 128) != 0 || (!trans_rhs && (n % 16) != 0)) return RD_EUNSUPPORTED;
   if (k * (m > n ? m : n) >= (int64_t(1) << 32)) return RD_EUNSUPPORTED;
   st = check_groups(num_groups, group_offset, num_local);
   if (st != RD_OK) return st;
@@ -170,7 +171,22 @@ int rd_forward_trans_rhs_fp8(const void* x, const void* w, const int32_t* group_
   p.m = static_cast<int>(m);
   p.k = static_cast<int>(k);
   p.n = static_cast<int>(n);
-  return rd::launch_forward_fp8_trans_rhs(p, static_cast<hipStream_t>(stream));
+  return rd::launch_forward_fp8(p, trans_rhs, static_cast<hipStream_t>(stream));
+}
+}  // namespace
+
+int rd_forward_fp8(const void* x, const void* w, const int32_t* group_sizes, int32_t num_groups,
+                   const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* out,
+                   int32_t out_dtype, int64_t m, int64_t k, int64_t n, void* stream) {
+  return forward_fp8(x, w, group_sizes, num_groups, group_offset, num_local, limit, out, out_dtype, m, k, n, stream,
+                     false);
+}
+
+int rd_forward_trans_rhs_fp8(const void* x, const void* w, const int32_t* group_sizes, int32_t num_groups,
+                             const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* out,
+                             int32_t out_dtype, int64_t m, int64_t k, int64_t n, void* stream) {
+  return forward_fp8(x, w, group_sizes, num_groups, group_offset, num_local, limit, out, out_dtype, m, k, n, stream,
+                     true);
 }
 
 size_t rd_trans_workspace_size(int64_t m, int64_t k, int64_t n, int32_t num_local) {

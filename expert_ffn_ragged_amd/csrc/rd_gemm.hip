@@ -42,7 +42,7 @@
 namespace rd {
 namespace {
 
-enum Mode { kFwdNN = 0, kFwdNT = 1, kTransTN = 2, kFwdNT8 = 3, kFwdGLU = 4 };
+enum Mode { kFwdNN = 0, kFwdNT = 1, kTransTN = 2, kFwdNT8 = 3, kFwdGLU = 4, kFwdNN8 = 5 };
 
 constexpr int BK = 64;  // contraction elements per pipeline stage
 constexpr int kZeroRows = 16;
@@ -819,8 +819,38 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_regs(KArgs p) {
 // (KS 16-bit elements = 2 * KS fp8 per stage row), only the fragment differs.
 template <int ROWS, int KS, int NW = 4>
 struct K8Dma : KDma<ROWS, KS, NW> {
+  static constexpr int kFrag8Reads = 2;
   __device__ __forceinline__ static i32x8_t frag8(const uint16_t* tile, int r_base, int kk) {
     return KLayoutT<KS>::frag8(tile, r_base, kk);
+  }
+};
+
+// fp8 MN-contiguous operand (the weight w [k, n] of the plain form): a stage
+// is 2 * KS contraction rows of COLS fp8, moved as COLS / 2 16-bit elements
+// by the bf16 machinery (MNLayout<COLS / 2> rows).  The fragment comes
+// through the gfx950 8-bit LDS transpose read: within each 16-lane group,
+// lanes 2e and 2e+1 name row e of an 8 x 16-byte block (bytes 0..7 and 8..15)
+// and lane i receives byte i of each of the 8 rows (measured on the GPU).
+// Four reads give lane l the 32 contraction rows 64*kk + 32*(l/32) .. +31 of
+// column c_base + l % 32, in the order KLayoutT::frag8 gives the other
+// operand.
+template <int COLS, int KS, int NW = 4>
+struct MN8Dma : MNDma<COLS / 2, 2 * KS, NW> {
+  static constexpr int kFrag8Reads = 4;
+  __device__ __forceinline__ static i32x8_t frag8(const uint16_t* tile, int c_base, int kk) {
+    const int l = threadIdx.x & 63;
+    const int q = l & 15;
+    const int col = c_base + 16 * ((l >> 4) & 1) + 8 * (q & 1);  // fp8 column of this lane's 8 bytes
+    const int row0 = 64 * kk + 32 * (l >> 5) + (q >> 1);
+    typedef int i32x2_t __attribute__((ext_vector_type(2)));
+    i32x2_t r[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const unsigned char* p = reinterpret_cast<const unsigned char*>(
+                                   tile + MNLayout<COLS / 2>::offset(row0 + 8 * j, col >> 4)) + (col & 15);
+      r[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(RD_LDS(i32x2_t, p));
+    }
+    return i32x8_t{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
   }
 };
 
@@ -878,7 +908,8 @@ __device__ __forceinline__ void mma_stage8(const uint16_t* ta, const uint16_t* t
       for (int ni = 0; ni < NI; ++ni)
         acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[cur][mi], bfr[cur][ni], acc[mi][ni], 0, 0,
                                                                       0, 0, 0, 0);
-    if (kk + 1 < kSlices) __builtin_amdgcn_sched_group_barrier(0x100, 2 * (MI + NI), 0);
+    if (kk + 1 < kSlices)
+      __builtin_amdgcn_sched_group_barrier(0x100, OpA::kFrag8Reads * MI + OpB::kFrag8Reads * NI, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, MI * NI, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -914,6 +945,17 @@ struct StreamOps<kFwdNT8, BM, BN, KS, NW> {
   using B = K8Dma<BN, KS, NW>;
   __device__ __forceinline__ static void make(const KArgs& p, const FwdTiles::Tile& t, int wave, A& a, B& b) {
     StreamOps<kFwdNT, BM, BN, KS, NW>::make(p, t, wave, a, b);
+  }
+};
+// fp8 plain form: x [m, k] as k / 2 16-bit elements per row (KArgs::k) and
+// w [g, k, n] as 2 * KArgs::k rows of n / 2 16-bit elements.
+template <int BM, int BN, int KS, int NW>
+struct StreamOps<kFwdNN8, BM, BN, KS, NW> {
+  using A = K8Dma<BM, KS, NW>;
+  using B = MN8Dma<BN, KS, NW>;
+  __device__ __forceinline__ static void make(const KArgs& p, const FwdTiles::Tile& t, int wave, A& a, B& b) {
+    a.init(p.a + static_cast<long long>(t.row0) * p.k, t.row_end - t.row0, p.k, wave);
+    b.init(p.b + static_cast<long long>(t.j) * p.k * p.n, 2 * p.k, p.n / 2, t.n0 / 2, wave);
   }
 };
 template <int BM, int BN, int KS, int NW>
@@ -1062,7 +1104,7 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       const uint16_t* slot = s_tiles + (g % S) * ST;
-      if constexpr (MODE == kFwdNT8) {
+      if constexpr (MODE == kFwdNT8 || MODE == kFwdNN8) {
         produce();
         __builtin_amdgcn_sched_barrier(0);
         mma_stage8<OpA, OpB, MI, NI, KS>(slot, slot + A_EL, acc, wm_off, wn_off);
@@ -1540,14 +1582,17 @@ int launch_forward_glu(const GemmProblem& p, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? RD_OK : RD_EHIP;
 }
 
-int launch_forward_fp8_trans_rhs(const GemmProblem& p, hipStream_t stream) {
-  // the kernel addresses fp8 rows as k / 2 16-bit elements
+int launch_forward_fp8(const GemmProblem& p, bool trans_rhs, hipStream_t stream) {
+  // the kernels address fp8 rows as k / 2 16-bit elements
   GemmProblem q = p;
   q.k = p.k / 2;
   const KArgs a = make_args(q);
   const long long work = (static_cast<long long>((p.m + 127) / 128) + p.num_local) * ((p.n + 255) / 256) +
                          (p.m + kZeroRows - 1) / kZeroRows + 2;
-  launch_one<kFwdNT8, 128, 256, 3, 64>(a, work, stream);
+  if (trans_rhs)
+    launch_one<kFwdNT8, 128, 256, 3, 64>(a, work, stream);
+  else
+    launch_one<kFwdNN8, 128, 256, 3, 64>(a, work, stream);
   return hipGetLastError() == hipSuccess ? RD_OK : RD_EHIP;
 }
 

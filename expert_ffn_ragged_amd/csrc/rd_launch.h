@@ -36,8 +36,9 @@ DecodePlan plan_decode(const GemmProblem& p, bool trans_rhs);
 int launch_forward(const GemmProblem& p, bool trans_rhs, void* workspace, size_t workspace_bytes,
                    hipStream_t stream);
 int launch_trans(const GemmProblem& p, hipStream_t stream);
-// fp8 (OCP E4M3) x [m, k] and w [g, n, k]; requires k % 128 == 0 and k * max(m, n) < 2^32.
-int launch_forward_fp8_trans_rhs(const GemmProblem& p, hipStream_t stream);
+// fp8 (OCP E4M3) x [m, k] and w [g, n, k] (trans_rhs) or [g, k, n]; requires k % 128 == 0,
+// n % 16 == 0 and k * max(m, n) < 2^32.
+int launch_forward_fp8(const GemmProblem& p, bool trans_rhs, hipStream_t stream);
 // ragged_dot(x, w) with the GLU as its epilogue; requires k % 64 == 0, n (= h) % 128 == 0 and
 // operands under 4 GiB (fused_glu_supported).
 bool fused_glu_supported(const GemmProblem& p);

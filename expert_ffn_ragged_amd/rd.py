@@ -18,7 +18,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librd.so")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 RD_OK, RD_EINVAL, RD_EUNSUPPORTED, RD_EHIP = 0, 1, 2, 3
 RD_BF16, RD_F32 = 0, 1
 _DTYPES = {torch.bfloat16: RD_BF16, torch.float32: RD_F32}
@@ -30,6 +30,7 @@ EXPORTS = (
     "rd_forward",
     "rd_forward_trans_rhs",
     "rd_forward_trans_rhs_fp8",
+    "rd_forward_fp8",
     "rd_forward_glu",
     "rd_trans_workspace_size",
     "rd_trans",
@@ -67,6 +68,7 @@ def library():
         getattr(lib, name).argtypes = fwd
     lib.rd_forward_trans_rhs_fp8.restype = ctypes.c_int
     lib.rd_forward_trans_rhs_fp8.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, i32, i64, i64, i64, vp]
+    lib.rd_forward_fp8.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, i32, i64, i64, i64, vp]
     lib.rd_forward_glu.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, vp, i64, i64, i64, vp]
     lib.rd_trans_workspace_size.restype = sz
     lib.rd_trans_workspace_size.argtypes = [i64, i64, i64, i32]
@@ -162,11 +164,12 @@ def ragged_dot(x, w, group_sizes, group_offset=None, limit=None, trans_rhs=False
     return out
 
 
-def ragged_dot_fp8(x, w, group_sizes, group_offset=None, limit=None, out_dtype=torch.bfloat16, out=None,
-                   stream=None):
-    """fp8 (E4M3) ragged_dot in the trans_rhs form: out[rows of local group j] = x[rows] @ w[j].T.
+def ragged_dot_fp8(x, w, group_sizes, group_offset=None, limit=None, trans_rhs=False, out_dtype=torch.bfloat16,
+                   out=None, stream=None):
+    """fp8 (E4M3) ragged_dot: out[rows of local group j] = x[rows] @ w[j] (trans_rhs: @ w[j].T).
 
-    x: [m, k] torch.float8_e4m3fn; w: [num_local, n, k] torch.float8_e4m3fn; float32 accumulation.
+    x: [m, k] torch.float8_e4m3fn; w: [num_local, k, n] (trans_rhs: [num_local, n, k]) float8_e4m3fn;
+    float32 accumulation, one rounding to out_dtype.
     """
     _need(x, "x", torch.float8_e4m3fn, 2)
     _need(w, "w", torch.float8_e4m3fn, 3)
@@ -174,7 +177,10 @@ def ragged_dot_fp8(x, w, group_sizes, group_offset=None, limit=None, out_dtype=t
     group_offset = _scalar(group_offset, "group_offset")
     limit = _scalar(limit, "limit")
     m, k = x.shape
-    gl, n, kw = w.shape
+    if trans_rhs:
+        gl, n, kw = w.shape
+    else:
+        gl, kw, n = w.shape
     if kw != k:
         raise ValueError("contraction sizes of x and w differ")
     if out is None:
@@ -182,9 +188,9 @@ def ragged_dot_fp8(x, w, group_sizes, group_offset=None, limit=None, out_dtype=t
     _need(out, "out", out.dtype, 2)
     if tuple(out.shape) != (m, n) or out.dtype not in _DTYPES:
         raise ValueError("out must be [m, n] bf16 or float32")
-    _check(library().rd_forward_trans_rhs_fp8(_ptr(x), _ptr(w), _ptr(group_sizes), group_sizes.numel(),
-                                              _ptr(group_offset), gl, _ptr(limit), _ptr(out), _DTYPES[out.dtype],
-                                              m, k, n, _stream(stream)))
+    fn = library().rd_forward_trans_rhs_fp8 if trans_rhs else library().rd_forward_fp8
+    _check(fn(_ptr(x), _ptr(w), _ptr(group_sizes), group_sizes.numel(), _ptr(group_offset), gl, _ptr(limit),
+              _ptr(out), _DTYPES[out.dtype], m, k, n, _stream(stream)))
     return out
 
 

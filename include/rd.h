@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define RD_ABI_VERSION 3
+#define RD_ABI_VERSION 4
 
 /* status codes */
 #define RD_OK 0
@@ -145,6 +145,19 @@ int rd_forward_trans_rhs(const void* x, const void* w, const int32_t* group_size
 int rd_forward_trans_rhs_fp8(const void* x, const void* w, const int32_t* group_sizes, int32_t num_groups,
                              const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* out,
                              int32_t out_dtype, int64_t m, int64_t k, int64_t n, void* stream);
+
+/*
+ * ragged_dot on fp8 operands in the plain form ([SkyRL] ragged_dot with a
+ * compute_dtype, as rd_forward_trans_rhs_fp8): x [m, k] and
+ * w [num_local, k, n] hold OCP FP8 E4M3 values, out[r,:] = x[r,:] @ w[j]
+ * with float32 accumulation of the exact products, one rounding to
+ * out_dtype, no scaling factors.  Window, limit and row rules are those of
+ * rd_forward.  Requires k a multiple of 128, n a multiple of 16 and
+ * k * max(m, n) < 2^32 (else RD_EUNSUPPORTED).
+ */
+int rd_forward_fp8(const void* x, const void* w, const int32_t* group_sizes, int32_t num_groups,
+                   const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* out,
+                   int32_t out_dtype, int64_t m, int64_t k, int64_t n, void* stream);
 
 /*
  * trans_ragged_dot ([SkyRL], _gpu_trans_ragged_dot_fwd; the weight

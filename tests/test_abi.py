@@ -46,7 +46,7 @@ def test_links_the_same_hip_runtime_soname_as_torch():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.rd_abi_version() == rd.ABI_VERSION == 3
+    assert lib.rd_abi_version() == rd.ABI_VERSION == 4
     for s in (0, 1, 2, 3, 99):
         assert isinstance(lib.rd_status_string(s), bytes)
     assert lib.rd_trans_workspace_size(100, 64, 64, 4) == 0
@@ -152,3 +152,16 @@ def test_forward_glu_rejects_bad_arguments(lib):
     assert call(x=40) == rd.RD_EINVAL              # misaligned
     assert call(gl=5, off=16) == rd.RD_EINVAL      # num_local > num_groups
     assert call(m=0, x=None, act=None) == rd.RD_OK  # nothing to do, nothing launched
+
+
+def test_fp8_forms_reject_bad_sizes(lib):
+    """fp8 ragged_dot: k a multiple of 128 for both forms, n a multiple of 16 for the plain form."""
+    v = ctypes.c_void_p
+
+    def call(fn, k=128, n=32, m=8):
+        return fn(v(16), v(16), v(16), 1, None, 1, None, v(16), 0, m, k, n, None)
+    for fn in (lib.rd_forward_fp8, lib.rd_forward_trans_rhs_fp8):
+        assert call(fn, k=64) == rd.RD_EUNSUPPORTED
+        assert call(fn, k=0) == rd.RD_EINVAL
+        assert call(fn, m=0) == rd.RD_OK
+    assert call(lib.rd_forward_fp8, n=24) == rd.RD_EUNSUPPORTED

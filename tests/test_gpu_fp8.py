@@ -1,4 +1,4 @@
-"""GPU parity of the fp8 (E4M3) trans_rhs ragged_dot against the oracle.
+"""GPU parity of the fp8 (E4M3) ragged_dot, plain and trans_rhs forms, against the oracle.
 
 The oracle accumulates the exact products in float64; the kernel in
 float32 through the fp8 MFMA, so the GEMM tolerance applies.  Every E4M3
@@ -34,27 +34,28 @@ def codes(t):
     return t.detach().cpu().contiguous().view(torch.uint8).numpy()
 
 
+@pytest.mark.parametrize("trans_rhs", [True, False])
 @pytest.mark.parametrize("off,limit", [(None, None), (1, None), (None, 300), (2, 250)])
-def test_fp8_trans_rhs_small(off, limit):
-    say(f"fp8 trans_rhs off={off} limit={limit}")
+def test_fp8_small(off, limit, trans_rhs):
+    say(f"fp8 trans_rhs={trans_rhs} off={off} limit={limit}")
     gs_host = np.array([70, 0, 150, 5, 129, 0, 30], dtype=np.int32)
     m, k, n = int(gs_host.sum()) + 9, 384, 320
     gl = 7 if off is None else 4
     x = fp8_normal((m, k), 1.0, 11)
-    w = fp8_normal((gl, n, k), 0.5, 12)
+    w = fp8_normal((gl, n, k) if trans_rhs else (gl, k, n), 0.5, 12)
     gs = torch.from_numpy(gs_host).to(DEV)
     offt = None if off is None else dev_i32(off)
     limt = None if limit is None else dev_i32(limit)
     o32 = sentinel((m, n), torch.float32)
     o16 = sentinel((m, n), torch.bfloat16)
-    rd.ragged_dot_fp8(x, w, gs, offt, limt, out=o32)
-    rd.ragged_dot_fp8(x, w, gs, offt, limt, out=o16)
+    rd.ragged_dot_fp8(x, w, gs, offt, limt, trans_rhs=trans_rhs, out=o32)
+    rd.ragged_dot_fp8(x, w, gs, offt, limt, trans_rhs=trans_rhs, out=o16)
     # the bf16 kernel on the same (widened) values
-    ob = rd.ragged_dot(x.to(torch.bfloat16), w.to(torch.bfloat16), gs, offt, limt, trans_rhs=True,
+    ob = rd.ragged_dot(x.to(torch.bfloat16), w.to(torch.bfloat16), gs, offt, limt, trans_rhs=trans_rhs,
                        out_dtype=torch.float32)
     torch.cuda.synchronize()
     lb, lo, hi, L = oracle.boundaries(gs_host, m, off, gl, limit)
-    ref = oracle.ragged_dot_fp8(codes(x), codes(w), gs_host, off, limit)
+    ref = oracle.ragged_dot_fp8(codes(x), codes(w), gs_host, off, limit, trans_rhs=trans_rhs)
     assert_gemm_close(o32[:L].cpu().numpy(), ref, "fp8")
     assert_gemm_close(ob[:L].cpu().numpy(), ref, "bf16 of fp8 values")
     outside = torch.ones(L, dtype=torch.bool, device=DEV)
@@ -72,7 +73,7 @@ def test_fp8_moe_backward_shape_sampled():
     m, n, k = 32768, 1024, 4096
     x = fp8_normal((m, k), 1.0, 21)
     w = fp8_normal((64, n, k), 0.05, 22)
-    o32 = rd.ragged_dot_fp8(x, w, d["gs"], out_dtype=torch.float32)
+    o32 = rd.ragged_dot_fp8(x, w, d["gs"], trans_rhs=True, out_dtype=torch.float32)
     torch.cuda.synchronize()
     rng = np.random.default_rng(3)
     rows = np.unique(np.concatenate([rng.integers(0, m, size=96), [0, m - 1]]))
@@ -82,3 +83,27 @@ def test_fp8_moe_backward_shape_sampled():
     xs = codes(x[torch.from_numpy(rows).to(DEV)])
     ref = oracle.ragged_dot_fp8(xs, codes(w), counts)
     assert_gemm_close(o32[torch.from_numpy(rows).to(DEV)].cpu().numpy(), ref, "fp8 backward shape")
+
+
+def test_fp8_plain_up_projection_sampled():
+    """The up-projection (m8192, w[64, 4096, 2048], Zipf groups) in the plain form with fp8 operands,
+    sampled rows against the oracle; all rows against the bf16 kernel on the widened values."""
+    say("fp8 plain up-projection")
+    d = workloads.make(2, DEV, parts=())
+    gs_host = d["gs_host"]
+    m, k, n = 8192, 4096, 2048
+    x = fp8_normal((m, k), 1.0, 31)
+    w = fp8_normal((64, k, n), 0.05, 32)
+    o32 = rd.ragged_dot_fp8(x, w, d["gs"], out_dtype=torch.float32)
+    ob = rd.ragged_dot(x.to(torch.bfloat16), w.to(torch.bfloat16), d["gs"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    err = (o32 - ob).norm() / ob.norm()
+    assert float(err) <= 1e-5, f"fp8 vs bf16 kernel on the same values: {float(err):.2e}"
+    rng = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([rng.integers(0, m, size=64), [0, m - 1]]))
+    lb = np.concatenate([[0], np.cumsum(gs_host)])
+    owner = np.searchsorted(lb, rows, side="right") - 1
+    counts = np.bincount(owner, minlength=64).astype(np.int32)
+    xs = codes(x[torch.from_numpy(rows).to(DEV)])
+    ref = oracle.ragged_dot_fp8(xs, codes(w), counts, trans_rhs=False)
+    assert_gemm_close(o32[torch.from_numpy(rows).to(DEV)].cpu().numpy(), ref, "fp8 plain up-projection")
