@@ -20,7 +20,7 @@ from .bf16 import bf16_bits_to_f32, bf16_bits_to_f64, f32_to_bf16_bits
 from .ragged import boundaries, ragged_dot, trans_ragged_dot
 from .glu import glu_fwd, glu_bwd
 from .unsort import unsort_bwd_rows
-from .fp8 import e4m3_to_f64, e4m3_to_bf16_bits, ragged_dot_fp8
+from .fp8 import e4m3_to_f64, e4m3_to_bf16_bits, ragged_dot_fp8, trans_ragged_dot_fp8
 
 __all__ = [
     "bf16_bits_to_f32",
@@ -35,4 +35,5 @@ __all__ = [
     "e4m3_to_f64",
     "e4m3_to_bf16_bits",
     "ragged_dot_fp8",
+    "trans_ragged_dot_fp8",
 ]

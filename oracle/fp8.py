@@ -16,7 +16,7 @@ the fp8 ragged_dot reuses the bf16 one.
 import numpy as np
 
 from .bf16 import f32_to_bf16_bits
-from .ragged import ragged_dot
+from .ragged import ragged_dot, trans_ragged_dot
 
 
 def e4m3_to_f64(codes):
@@ -42,3 +42,12 @@ def ragged_dot_fp8(x, w, group_sizes, group_offset=None, limit=None, trans_rhs=T
     """
     return ragged_dot(e4m3_to_bf16_bits(x), e4m3_to_bf16_bits(w), group_sizes, group_offset, limit,
                       trans_rhs=trans_rhs)
+
+
+def trans_ragged_dot_fp8(x, y, group_sizes, num_local=None, group_offset=None, limit=None):
+    """trans_ragged_dot on E4M3 inputs: x uint8 [m, k], y uint8 [m, n] -> float64 [num_local, k, n].
+
+    Exactly the bf16 trans_ragged_dot of the same values (the products are exact in float64).
+    """
+    return trans_ragged_dot(e4m3_to_bf16_bits(x), e4m3_to_bf16_bits(y), group_sizes, num_local, group_offset,
+                            limit)

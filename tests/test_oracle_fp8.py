@@ -79,3 +79,26 @@ def test_single_group_is_dense_matmul():
     xt = torch.from_numpy(x).view(torch.float8_e4m3fn).to(torch.float64)
     wt = torch.from_numpy(w[0]).view(torch.float8_e4m3fn).to(torch.float64)
     assert np.allclose(got, (xt @ wt.T).numpy(), rtol=1e-15, atol=0)
+
+
+def test_trans_ragged_dot_fp8_brute_force():
+    """dw[j][a, c] = sum over group j's rows of x[r, a] * y[r, c], with torch's own E4M3 decode; an empty
+    group gives +0; rows past the limit and outside the window contribute nothing."""
+    rng = np.random.default_rng(7)
+    gs = np.array([4, 0, 3, 5], dtype=np.int32)
+    m, k, n = 13, 5, 6
+    x = _codes((m, k), rng)
+    y = _codes((m, n), rng)
+    got = ofp8.trans_ragged_dot_fp8(x, y, gs, num_local=3, group_offset=1, limit=10)
+    xv = torch.from_numpy(x).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    yv = torch.from_numpy(y).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    lb = np.minimum(np.concatenate([[0], np.cumsum(gs)]), 10)
+    assert got.shape == (3, k, n)
+    for j in range(3):
+        want = np.zeros((k, n))
+        for r in range(lb[1 + j], lb[2 + j]):
+            for a in range(k):
+                for c in range(n):
+                    want[a, c] += xv[r, a] * yv[r, c]
+        assert np.array_equal(got[j], want), j
+    assert np.all(got[0] == 0) and not np.signbit(got[0]).any()
