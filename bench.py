@@ -215,14 +215,18 @@ def extra_all(steps):
         out[f"backward_m32768_{key}"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1),
                                         "mfma_frac": round(fl / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
     # the same dx with fp8 (E4M3) operands
-    dy8, w8 = d["dy"].to(torch.float8_e4m3fn), d["w"].to(torch.float8_e4m3fn)
+    dy8, w8, x8 = d["dy"].to(torch.float8_e4m3fn), d["w"].to(torch.float8_e4m3fn), d["x"].to(torch.float8_e4m3fn)
     del d, dw, dw32
     torch.cuda.empty_cache()
     out.update(glu_epilogue(steps))
     _, _, per = timed_ops([("dx_fp8", lambda: rd.ragged_dot_fp8(dy8, w8, gs3, trans_rhs=True, out=dx))], steps, 3)
-    out["backward_m32768_dx_fp8"] = {"ms": round(per["dx_fp8"], 4), "TFLOP/s": round(fl / per["dx_fp8"] / 1e9, 1),
-                                     "mfma_frac_fp8": round(fl / per["dx_fp8"] / 1e9 / MFMA_FP8_PEAK_TFLOPS, 4)}
-    del dy8, w8, dx
+    dw8 = torch.empty((64, k, n), dtype=torch.bfloat16, device="cuda")
+    _, _, per2 = timed_ops([("dw_fp8", lambda: rd.trans_ragged_dot_fp8(x8, dy8, gs3, out=dw8))], steps, 3)
+    per.update(per2)
+    for key in ("dx_fp8", "dw_fp8"):
+        out[f"backward_m32768_{key}"] = {"ms": round(per[key], 4), "TFLOP/s": round(fl / per[key] / 1e9, 1),
+                                        "mfma_frac_fp8": round(fl / per[key] / 1e9 / MFMA_FP8_PEAK_TFLOPS, 4)}
+    del dy8, w8, x8, dx, dw8
     torch.cuda.empty_cache()
     d = workloads.make(4, "cuda", parts=("x", "w", "fused", "d_out"))
     off = torch.tensor([96], dtype=torch.int32, device="cuda")

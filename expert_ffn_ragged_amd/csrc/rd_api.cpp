@@ -197,6 +197,38 @@ size_t rd_trans_workspace_size(int64_t m, int64_t k, int64_t n, int32_t num_loca
   return 0;  // every dw tile is reduced by one workgroup: no partials to stage
 }
 
+int rd_trans_fp8(const void* x, const void* dy, const int32_t* group_sizes, int32_t num_groups,
+                 const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* dw,
+                 int32_t dw_dtype, int64_t m, int64_t k, int64_t n, void* stream) {
+  int st = check_dims(m, k, n);
+  if (st != RD_OK) return st;
+  if ((k % 16) != 0 || (n % 16) != 0) return RD_EUNSUPPORTED;
+  if (m * (k > n ? k : n) >= (int64_t(1) << 32)) return RD_EUNSUPPORTED;
+  st = check_groups(num_groups, group_offset, num_local);
+  if (st != RD_OK) return st;
+  if (dw_dtype != RD_BF16 && dw_dtype != RD_F32) return RD_EINVAL;
+  if (!group_sizes || !dw) return RD_EINVAL;
+  if (m > 0 && (!x || !dy)) return RD_EINVAL;  // no rows: x and dy may be empty (null)
+  if ((m > 0 && (!aligned16(x) || !aligned16(dy))) || !aligned16(dw)) return RD_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(group_sizes) & 3u) || (reinterpret_cast<uintptr_t>(limit) & 3u) ||
+      (reinterpret_cast<uintptr_t>(group_offset) & 3u))
+    return RD_EINVAL;
+  rd::GemmProblem p{};
+  p.a = x;
+  p.b = dy;
+  p.group_sizes = group_sizes;
+  p.num_groups = num_groups;
+  p.group_offset = group_offset;
+  p.num_local = num_local;
+  p.limit = limit;
+  p.out = dw;
+  p.out_f32 = dw_dtype == RD_F32;
+  p.m = static_cast<int>(m);
+  p.k = static_cast<int>(k);
+  p.n = static_cast<int>(n);
+  return rd::launch_trans_fp8(p, static_cast<hipStream_t>(stream));
+}
+
 int rd_trans(const void* x, const void* dy, const int32_t* group_sizes, int32_t num_groups,
              const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* dw,
              int32_t dw_dtype, int64_t m, int64_t k, int64_t n, void* workspace,

@@ -42,7 +42,9 @@
 namespace rd {
 namespace {
 
-enum Mode { kFwdNN = 0, kFwdNT = 1, kTransTN = 2, kFwdNT8 = 3, kFwdGLU = 4, kFwdNN8 = 5 };
+enum Mode { kFwdNN = 0, kFwdNT = 1, kTransTN = 2, kFwdNT8 = 3, kFwdGLU = 4, kFwdNN8 = 5, kTransTN8 = 6 };
+constexpr bool is_trans(int mode) { return mode == kTransTN || mode == kTransTN8; }
+constexpr bool is_fp8(int mode) { return mode == kFwdNT8 || mode == kFwdNN8 || mode == kTransTN8; }
 
 constexpr int BK = 64;  // contraction elements per pipeline stage
 constexpr int kZeroRows = 16;
@@ -958,6 +960,17 @@ struct StreamOps<kFwdNN8, BM, BN, KS, NW> {
     b.init(p.b + static_cast<long long>(t.j) * p.k * p.n, 2 * p.k, p.n / 2, t.n0 / 2, wave);
   }
 };
+// fp8 trans_ragged_dot: x [m, k] and dy [m, n] as fp8 rows of k / 2 and
+// n / 2 16-bit elements; a stage is 2 * KS rows of the group.
+template <int BM, int BN, int KS, int NW>
+struct StreamOps<kTransTN8, BM, BN, KS, NW> {
+  using A = MN8Dma<BM, KS, NW>;
+  using B = MN8Dma<BN, KS, NW>;
+  __device__ __forceinline__ static void make(const KArgs& p, const TransTiles::Tile& t, int wave, A& a, B& b) {
+    a.init(p.a + static_cast<long long>(t.r_begin) * (p.k / 2), t.r_end - t.r_begin, p.k / 2, t.a0 / 2, wave);
+    b.init(p.b + static_cast<long long>(t.r_begin) * (p.n / 2), t.r_end - t.r_begin, p.n / 2, t.c0 / 2, wave);
+  }
+};
 template <int BM, int BN, int KS, int NW>
 struct StreamOps<kTransTN, BM, BN, KS, NW> {
   using A = MNDma<BM, KS, NW>;
@@ -1012,7 +1025,9 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
   using Ops = StreamOps<MODE, BM, BN, KS, NW>;
   using OpA = typename Ops::A;
   using OpB = typename Ops::B;
-  using Tiles = typename std::conditional<MODE == kTransTN, TransTiles, FwdTiles>::type;
+  using Tiles = typename std::conditional<is_trans(MODE), TransTiles, FwdTiles>::type;
+  // contraction rows per stage in the tile lists (fp8 trans: 2 * KS rows of fp8 per stage)
+  constexpr int KSTEP = MODE == kTransTN8 ? 2 * KS : KS;
   constexpr int L = OpA::kInstr + OpB::kInstr;  // loads per wave per step
   __shared__ __attribute__((aligned(1024))) uint16_t s_tiles[S * ST];
   __shared__ int s_lb[MAXL + 1];
@@ -1024,7 +1039,7 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
   const Window win = build_local_bounds<NT>(p.gs, p.G, p.offp, p.gl, p.limp, p.m, s_lb, s_wave);
 
   Tiles tl;
-  if constexpr (MODE == kTransTN) {
+  if constexpr (is_trans(MODE)) {
     order_groups<NT>(s_lb, p.gl, s_aux);
     tl.init(p.gl, p.k, p.n, BM, BN);
   } else {
@@ -1032,8 +1047,8 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
     tl.init(total_m, p.n, TN, p.k);
   }
   auto tile_at = [&](long long s, typename Tiles::Tile& t) -> bool {
-    if constexpr (MODE == kTransTN)
-      return tl.template get<BM, BN, KS>(s, s_lb, s_aux, t);
+    if constexpr (is_trans(MODE))
+      return tl.template get<BM, BN, KSTEP>(s, s_lb, s_aux, t);
     else
       return tl.template get<BM, TN, KS>(s, s_lb, s_aux, p.gl, p.k, t);
   };
@@ -1078,7 +1093,7 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
     if (!tile_at(cs, t)) continue;
     char* out;
     int r0, rlim, c0;
-    if constexpr (MODE == kTransTN) {
+    if constexpr (is_trans(MODE)) {
       out = static_cast<char*>(p.out) + static_cast<long long>(t.j) * p.k * p.n * (p.out_f32 ? 4 : 2);
       r0 = t.a0 + wm_off;
       rlim = p.k;
@@ -1104,7 +1119,7 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       const uint16_t* slot = s_tiles + (g % S) * ST;
-      if constexpr (MODE == kFwdNT8 || MODE == kFwdNN8) {
+      if constexpr (is_fp8(MODE)) {
         produce();
         __builtin_amdgcn_sched_barrier(0);
         mma_stage8<OpA, OpB, MI, NI, KS>(slot, slot + A_EL, acc, wm_off, wn_off);
@@ -1127,7 +1142,7 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
     else
       store_wave_tile<MI, NI, EPI>(acc, out, p.out_f32, p.n, r0, rlim, c0, p.n, stage);
   }
-  if constexpr (MODE != kTransTN) zero_outside_window<NT>(p.out, p.n, p.out_f32 != 0, win);
+  if constexpr (!is_trans(MODE)) zero_outside_window<NT>(p.out, p.n, p.out_f32 != 0, win);
   if constexpr (MODE == kFwdGLU)
     if (p.out2 != nullptr) zero_outside_window<NT>(p.out2, 2 * p.n, false, win);
 }
@@ -1438,7 +1453,7 @@ void launch_one(const KArgs& a, long long work, hipStream_t stream) {
 template <int MODE>
 void launch_tile(int tile, const KArgs& a, const GemmProblem& p, hipStream_t stream) {
   auto work = [&](int BM, int BN) {
-    if (MODE == kTransTN)
+    if (is_trans(MODE))
       return static_cast<long long>(p.num_local) * ((p.k + BM - 1) / BM) * ((p.n + BN - 1) / BN);
     return (static_cast<long long>((p.m + BM - 1) / BM) + p.num_local) * ((p.n + BN - 1) / BN) +
            (p.m + kZeroRows - 1) / kZeroRows + 2;
@@ -1593,6 +1608,13 @@ int launch_forward_fp8(const GemmProblem& p, bool trans_rhs, hipStream_t stream)
     launch_one<kFwdNT8, 128, 256, 3, 64>(a, work, stream);
   else
     launch_one<kFwdNN8, 128, 256, 3, 64>(a, work, stream);
+  return hipGetLastError() == hipSuccess ? RD_OK : RD_EHIP;
+}
+
+int launch_trans_fp8(const GemmProblem& p, hipStream_t stream) {
+  const KArgs a = make_args(p);
+  launch_one<kTransTN8, 128, 256, 3, 64>(
+      a, static_cast<long long>(p.num_local) * ((p.k + 127) / 128) * ((p.n + 255) / 256), stream);
   return hipGetLastError() == hipSuccess ? RD_OK : RD_EHIP;
 }
 

@@ -18,7 +18,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librd.so")
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 RD_OK, RD_EINVAL, RD_EUNSUPPORTED, RD_EHIP = 0, 1, 2, 3
 RD_BF16, RD_F32 = 0, 1
 _DTYPES = {torch.bfloat16: RD_BF16, torch.float32: RD_F32}
@@ -34,6 +34,7 @@ EXPORTS = (
     "rd_forward_glu",
     "rd_trans_workspace_size",
     "rd_trans",
+    "rd_trans_fp8",
     "rd_glu_fwd",
     "rd_glu_bwd",
     "rd_unsort_bwd_rows",
@@ -74,6 +75,7 @@ def library():
     lib.rd_trans_workspace_size.argtypes = [i64, i64, i64, i32]
     lib.rd_trans.restype = ctypes.c_int
     lib.rd_trans.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, i32, i64, i64, i64, vp, sz, vp]
+    lib.rd_trans_fp8.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, i32, i64, i64, i64, vp]
     lib.rd_glu_fwd.restype = ctypes.c_int
     lib.rd_glu_fwd.argtypes = [vp, vp, vp, i64, i64, vp]
     lib.rd_glu_bwd.restype = ctypes.c_int
@@ -191,6 +193,32 @@ def ragged_dot_fp8(x, w, group_sizes, group_offset=None, limit=None, trans_rhs=F
     fn = library().rd_forward_trans_rhs_fp8 if trans_rhs else library().rd_forward_fp8
     _check(fn(_ptr(x), _ptr(w), _ptr(group_sizes), group_sizes.numel(), _ptr(group_offset), gl, _ptr(limit),
               _ptr(out), _DTYPES[out.dtype], m, k, n, _stream(stream)))
+    return out
+
+
+def trans_ragged_dot_fp8(x, dy, group_sizes, num_local=None, group_offset=None, limit=None,
+                         out_dtype=torch.float32, out=None, stream=None):
+    """fp8 (E4M3) trans_ragged_dot: dw[j] = x_j^T @ dy_j, float32 accumulation, one rounding to out_dtype.
+
+    x: [m, k] and dy: [m, n] torch.float8_e4m3fn; returns [num_local, k, n].
+    """
+    _need(x, "x", torch.float8_e4m3fn, 2)
+    _need(dy, "dy", torch.float8_e4m3fn, 2)
+    _need(group_sizes, "group_sizes", torch.int32, 1)
+    group_offset = _scalar(group_offset, "group_offset")
+    limit = _scalar(limit, "limit")
+    m, k = x.shape
+    if dy.shape[0] != m:
+        raise ValueError("x and dy row counts differ")
+    n = dy.shape[1]
+    gl = group_sizes.numel() if num_local is None else int(num_local)
+    if out is None:
+        out = torch.empty((gl, k, n), dtype=out_dtype, device=x.device)
+    _need(out, "out", out.dtype, 3)
+    if tuple(out.shape) != (gl, k, n) or out.dtype not in _DTYPES:
+        raise ValueError("out must be [num_local, k, n] bf16 or float32")
+    _check(library().rd_trans_fp8(_ptr(x), _ptr(dy), _ptr(group_sizes), group_sizes.numel(), _ptr(group_offset), gl,
+                                  _ptr(limit), _ptr(out), _DTYPES[out.dtype], m, k, n, _stream(stream)))
     return out
 
 

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define RD_ABI_VERSION 4
+#define RD_ABI_VERSION 5
 
 /* status codes */
 #define RD_OK 0
@@ -181,6 +181,19 @@ int rd_trans(const void* x, const void* dy, const int32_t* group_sizes, int32_t 
              const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* dw,
              int32_t dw_dtype, int64_t m, int64_t k, int64_t n, void* workspace,
              size_t workspace_bytes, void* stream);
+
+/*
+ * trans_ragged_dot on fp8 operands (as rd_trans; [SkyRL] compute_dtype, the
+ * reading of rd_forward_trans_rhs_fp8): x [m, k] and dy [m, n] hold OCP FP8
+ * E4M3 values, dw[j] = x_j^T @ dy_j with float32 accumulation of the exact
+ * products over the group's rows, one rounding to dw_dtype; rows outside a
+ * group removed by selection, an empty group +0, rows >= L never read.
+ * Requires k and n multiples of 16 and m * max(k, n) < 2^32 (else
+ * RD_EUNSUPPORTED).  No workspace.
+ */
+int rd_trans_fp8(const void* x, const void* dy, const int32_t* group_sizes, int32_t num_groups,
+                 const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* dw,
+                 int32_t dw_dtype, int64_t m, int64_t k, int64_t n, void* stream);
 
 /*
  * The MoE up-projection with the GLU as its epilogue ([MaxText]: the expert

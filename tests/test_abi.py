@@ -46,7 +46,7 @@ def test_links_the_same_hip_runtime_soname_as_torch():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.rd_abi_version() == rd.ABI_VERSION == 4
+    assert lib.rd_abi_version() == rd.ABI_VERSION == 5
     for s in (0, 1, 2, 3, 99):
         assert isinstance(lib.rd_status_string(s), bytes)
     assert lib.rd_trans_workspace_size(100, 64, 64, 4) == 0

@@ -107,3 +107,58 @@ def test_fp8_plain_up_projection_sampled():
     xs = codes(x[torch.from_numpy(rows).to(DEV)])
     ref = oracle.ragged_dot_fp8(xs, codes(w), counts, trans_rhs=False)
     assert_gemm_close(o32[torch.from_numpy(rows).to(DEV)].cpu().numpy(), ref, "fp8 plain up-projection")
+
+
+@pytest.mark.parametrize("off,limit", [(None, None), (1, None), (2, 250)])
+def test_fp8_trans_ragged_dot_small(off, limit):
+    """dw[j] = x_j^T dy_j on fp8 operands against the oracle (float32 output, GEMM tolerance), NaN rows past
+    the limit never reaching dw, an empty group +0, bf16 output = RNE of the float32 one."""
+    say(f"fp8 trans_ragged_dot off={off} limit={limit}")
+    gs_host = np.array([70, 0, 150, 5, 129, 0, 30], dtype=np.int32)
+    m, k, n = int(gs_host.sum()) + 9, 192, 320
+    gl = 7 if off is None else 4
+    x = fp8_normal((m, k), 1.0, 41)
+    y = fp8_normal((m, n), 1.0, 42)
+    if limit is not None:  # NaN codes past the limit must be removed by selection
+        x.view(torch.uint8)[limit:] = 0x7F
+        y.view(torch.uint8)[limit:] = 0x7F
+    gs = torch.from_numpy(gs_host).to(DEV)
+    offt = None if off is None else dev_i32(off)
+    limt = None if limit is None else dev_i32(limit)
+    d32 = sentinel((gl, k, n), torch.float32)
+    d16 = sentinel((gl, k, n), torch.bfloat16)
+    rd.trans_ragged_dot_fp8(x, y, gs, gl, offt, limt, out=d32)
+    rd.trans_ragged_dot_fp8(x, y, gs, gl, offt, limt, out=d16)
+    torch.cuda.synchronize()
+    ref = oracle.trans_ragged_dot_fp8(codes(x), codes(y), gs_host, gl, off, limit)
+    assert_gemm_close(d32.cpu().numpy(), ref, "fp8 trans")
+    assert_bf16_is_rne_of_f32(d16, d32, "fp8 trans")
+    lb, _, _, _ = oracle.boundaries(gs_host, m, off, gl, limit)
+    for j in range(gl):
+        if lb[j + 1] == lb[j]:
+            assert bool(is_pos_zero(d32[j]).all()) and bool(is_pos_zero(d16[j]).all()), j
+
+
+def test_fp8_trans_backward_shape_sampled():
+    """dW of the backward workload (x [32768, 1024], dy [32768, 4096], 64 groups, 4 empty) with fp8 operands:
+    every group's dW rows sampled against the oracle."""
+    say("fp8 trans_ragged_dot backward shape")
+    d = workloads.make(3, DEV, parts=())
+    gs_host = d["gs_host"]
+    m, k, n = 32768, 1024, 4096
+    x = fp8_normal((m, k), 1.0, 51)
+    y = fp8_normal((m, n), 1.0, 52)
+    dw = rd.trans_ragged_dot_fp8(x, y, d["gs"])
+    torch.cuda.synchronize()
+    lb = np.concatenate([[0], np.cumsum(gs_host)])
+    rng = np.random.default_rng(5)
+    a_rows = np.sort(rng.choice(k, size=3, replace=False))
+    xc, yc = codes(x), codes(y)
+    for j in range(64):
+        r0, r1 = int(lb[j]), int(lb[j + 1])
+        got = dw[j][torch.from_numpy(a_rows).to(DEV)].cpu().numpy()
+        if r1 == r0:
+            assert np.all(got == 0), j
+            continue
+        ref = oracle.trans_ragged_dot_fp8(xc[r0:r1][:, a_rows], yc[r0:r1], np.array([r1 - r0], dtype=np.int32))[0]
+        assert_gemm_close(got, ref, f"fp8 dW group {j}")
