@@ -210,10 +210,19 @@ def extra_all(steps):
         ("dw_bf16", lambda: rd.trans_ragged_dot(d["x"], d["dy"], d["gs"], out=dw)),
         ("dw_f32", lambda: rd.trans_ragged_dot(d["x"], d["dy"], d["gs"], out=dw32)),
     ], steps, 3)
+    # context: the vendor library's dense bf16 GEMM of the same flops (dy [m, n] times one expert's
+    # w [k, n] transposed, no grouping), through torch
+    wd = d["w"][0].contiguous()
+    _, _, per_d = timed_ops([("dense", lambda: torch.nn.functional.linear(d["dy"], wd))], steps, 3)
     fl = 2.0 * rows * k * n
     for key, ms in per.items():
         out[f"backward_m32768_{key}"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1),
                                         "mfma_frac": round(fl / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    fld = 2.0 * m * k * n
+    out["backward_m32768_dx_dense_torch_reference"] = {
+        "ms": round(per_d["dense"], 4), "TFLOP/s": round(fld / per_d["dense"] / 1e9, 1),
+        "mfma_frac": round(fld / per_d["dense"] / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    del wd
     # the same dx with fp8 (E4M3) operands
     dy8, w8, x8 = d["dy"].to(torch.float8_e4m3fn), d["w"].to(torch.float8_e4m3fn), d["x"].to(torch.float8_e4m3fn)
     del d, dw, dw32
