@@ -21,7 +21,7 @@ from tests.gpu_util import assert_bf16_is_rne_of_f32, assert_gemm_close, is_pos_
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
-TILE_SHAPES = list(range(17))
+TILE_SHAPES = list(range(18))
 
 GS = np.array([37, 0, 300, 129, 1, 200, 64], dtype=np.int32)
 M, K, N = int(GS.sum()) + 23, 320, 576
