@@ -105,8 +105,8 @@ def traffic_summary(fetch_dir, write_dir, mfma_dir, command):
     lines = [
         "# HBM traffic per launch: MoE up-projection fwd+bwd step (m8192 k4096 n2048 g64 Zipf 1.1), MI355X",
         "",
-        "Commands (from the repository root on the GPU box, `cd /tmp && export TMPDIR=/tmp` first; one",
-        "counter per run, each run its own process):",
+        "Commands (run from the repository root on the GPU box with `TMPDIR=/tmp` exported; one counter",
+        "per run, each run its own process):",
         "",
         "```",
         command,
@@ -150,8 +150,8 @@ def stats_summary(stats_dir, command, title):
             continue
         rows.append((short_name(row["Name"]), int(row["Calls"]), float(row["AverageNs"]) / 1e3,
                      float(row["MinNs"]) / 1e3, float(row["MaxNs"]) / 1e3))
-    lines = [f"# Kernel durations: {title}", "", "Command (from the repository root on the GPU box, "
-             "`cd /tmp && export TMPDIR=/tmp` first):", "", "```", command, "```", "",
+    lines = [f"# Kernel durations: {title}", "", "Command (run from the repository root on the GPU box "
+             "with `TMPDIR=/tmp` exported):", "", "```", command, "```", "",
              f"source digest: {source_digest()}", "",
              "| kernel | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
     for name, calls, avg, mn, mx in sorted(rows, key=lambda r: -r[2]):
