@@ -43,6 +43,8 @@ def parse():
                     help="flush L2 and the MALL (a 512 MiB write) before every timed step, outside the events")
     ap.add_argument("--copy-calib", action="store_true",
                     help="first copy 256 MiB device-to-device three times (reference kernel for HBM counters)")
+    ap.add_argument("--api-region", action="store_true",
+                    help="only run the marked region for a HIP API trace (see api_region) and exit")
     return ap.parse_args()
 
 
@@ -342,6 +344,64 @@ def mlp_layer(steps):
                                                      "mfma_frac": round(flop / per["mlp"] / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}}
 
 
+def api_region(iters=5):
+    """A region for a HIP API trace (rocprofv3 --hip-trace --memory-copy-trace): the decode layer
+    (ragged_dot -> GLU, eagerly and as a replayed graph, group_sizes rewritten on the device between
+    replays) and the up-projection step, ``iters`` times, between two hipMemGetInfo calls that mark it.
+    Everything is allocated and captured before the first mark; inside the region only the library's
+    calls and device-side copies run, so any copy to the host, synchronization or allocation the
+    trace shows there would be the library's."""
+    import torch
+
+    from expert_ffn_ragged_amd import rd, workloads
+
+    d5 = workloads.make(5, "cuda", parts=("x", "w"))
+    x5, w5, gs5 = d5["x"], d5["w"], d5["gs"]
+    m5, n5 = d5["m"], d5["n"]
+    gs_alt = torch.roll(gs5, 1)
+    gs_now = gs5.clone()
+    ws = torch.empty(max(rd.library().rd_forward_workspace_size(m5, d5["k"], n5, d5["G"], 0), 16),
+                     dtype=torch.uint8, device="cuda")
+    o5 = torch.empty((m5, n5), dtype=torch.bfloat16, device="cuda")
+    a5 = torch.empty((m5, n5 // 2), dtype=torch.bfloat16, device="cuda")
+
+    def decode_layer():
+        rd.ragged_dot(x5, w5, gs_now, out=o5, workspace=ws)
+        rd.glu_fwd(o5, out=a5)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        decode_layer()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        decode_layer()
+    d = workloads.make(2, "cuda", parts=("x", "w"))
+    x, w, gs = d["x"], d["w"], d["gs"]
+    m, k, n = d["m"], d["k"], d["n"]
+    d_act = workloads.bf16_normal((m, n // 2), 1.0, 2006, "cuda")
+    fused = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    act = torch.empty((m, n // 2), dtype=torch.bfloat16, device="cuda")
+    dfused = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    dx = torch.empty((m, k), dtype=torch.bfloat16, device="cuda")
+    dw = torch.empty((w.shape[0], k, n), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    torch.cuda.mem_get_info()  # region start mark
+    for i in range(iters):
+        decode_layer()
+        gs_now.copy_(gs_alt if i % 2 == 0 else gs5)  # device-to-device rewrite of group_sizes
+        graph.replay()
+        rd.ragged_dot(x, w, gs, out=fused)
+        rd.glu_fwd(fused, out=act)
+        rd.glu_bwd(fused, d_act, out=dfused)
+        rd.ragged_dot(dfused, w, gs, trans_rhs=True, out=dx)
+        rd.trans_ragged_dot(x, dfused, gs, out=dw)
+    torch.cuda.mem_get_info()  # region end mark
+    torch.cuda.synchronize()
+    print(json.dumps({"api_region": "done", "iters": iters}), flush=True)
+
+
 def cpu_baseline(x, w, dy, gs_host, budget_s=12.0):
     """The CPU oracle, as it stands, on a bounded sample of the timed workload.
 
@@ -399,6 +459,9 @@ def main():
     from expert_ffn_ragged_amd import rd
 
     rd.library()
+    if args.api_region:
+        api_region()
+        return
     COLD["on"] = args.cold
     if args.copy_calib:
         a = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")

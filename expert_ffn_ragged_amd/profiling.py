@@ -18,6 +18,7 @@ Usage (on the host, after copying the rocprofv3 output directories back)::
     python -m expert_ffn_ragged_amd.profiling traffic --fetch DIR --write DIR \\
         [--mfma DIR] --command "..." --out profiles/upproj_fwd_bwd_traffic.md
     python -m expert_ffn_ragged_amd.profiling stats --stats DIR --command "..." --out FILE.md
+    python -m expert_ffn_ragged_amd.profiling apitrace --trace DIR --command "..." --out FILE.md
 """
 
 import argparse
@@ -159,6 +160,63 @@ def stats_summary(stats_dir, command, title):
     return "\n".join(lines) + "\n"
 
 
+# HIP API calls that would break the no-host-sync property inside the marked region
+# (copies are judged by the memory-copy trace's direction: a device-to-device rewrite is allowed)
+SYNC_CALLS = re.compile(r"Synchronize|Malloc|Free|DtoH|Query|hipMemcpy$|WithStream")
+
+
+def apitrace_summary(trace_dir, command):
+    """HIP API calls, memory copies and kernels between the two hipMemGetInfo marks of
+    ``bench.py --api-region``, from a ``rocprofv3 --hip-trace --memory-copy-trace --kernel-trace`` run."""
+    api = list(_rows(trace_dir, "hip_api_trace.csv"))
+    marks = sorted(int(r["Start_Timestamp"]) for r in api if r["Function"] == "hipMemGetInfo")
+    if len(marks) < 2:
+        raise SystemExit("no pair of hipMemGetInfo marks in the trace")
+    t0, t1 = marks[-2], marks[-1]
+    inside = [r for r in api if t0 < int(r["Start_Timestamp"]) < t1]
+    calls = {}
+    for r in inside:
+        calls[r["Function"]] = calls.get(r["Function"], 0) + 1
+    copies = {}
+    for r in _rows(trace_dir, "memory_copy_trace.csv"):
+        if t0 < int(r["Start_Timestamp"]) < t1:
+            key = r.get("Direction") or r.get("Kind") or "copy"
+            copies[key] = copies.get(key, 0) + 1
+    # kernels dispatched by the region's calls (matched by correlation id; they may run after the mark)
+    ids = {r["Correlation_Id"] for r in inside}
+    kernels = {}
+    for r in _rows(trace_dir, "kernel_trace.csv"):
+        if r["Correlation_Id"] in ids:
+            name = short_name(r["Kernel_Name"])
+            kernels[name] = kernels.get(name, 0) + 1
+    bad = {f: c for f, c in calls.items() if SYNC_CALLS.search(f)}
+    to_host = {k: c for k, c in copies.items() if "HOST" in k.upper()}
+    lines = ["# HIP API trace of the library's calls: decode layer (eager and graph replays) and the "
+             "up-projection fwd+bwd step, MI355X", "",
+             "Command (run from the repository root on the GPU box with `TMPDIR=/tmp` exported):", "",
+             "```", command, "```", "",
+             "The region lies between the two `hipMemGetInfo` marks of `bench.py --api-region`: five rounds of "
+             "the decode layer (ragged_dot then GLU, eagerly), a device-to-device rewrite of group_sizes, a "
+             "replay of the same layer captured as a graph, and the five kernels of the up-projection step.", "",
+             f"source digest: {source_digest()}", "",
+             f"Synchronizations, allocations or blocking copies among the calls: **{sum(bad.values())}**"
+             + (f" ({bad})" if bad else "") + ".",
+             f"Memory copies to or from the host: **{sum(to_host.values())}**"
+             + (f" ({to_host})" if to_host else "") + ".", "",
+             "| HIP API call | calls in the region |", "|---|---|"]
+    for f, c in sorted(calls.items(), key=lambda kv: -kv[1]):
+        lines.append(f"| `{f}` | {c} |")
+    lines += ["", "| memory copy | count |", "|---|---|"]
+    for k, c in sorted(copies.items()):
+        lines.append(f"| {k} | {c} |")
+    if not copies:
+        lines.append("| none recorded (the group_sizes rewrites are copy kernels on the device) | 0 |")
+    lines += ["", "| kernel | dispatches by the region's calls |", "|---|---|"]
+    for k, c in sorted(kernels.items(), key=lambda kv: -kv[1]):
+        lines.append(f"| `{k}` | {c} |")
+    return "\n".join(lines) + "\n"
+
+
 def load_traffic(path):
     """{op: traffic bytes per launch} from a traffic summary whose digest matches the sources, else {}."""
     if not os.path.exists(path):
@@ -192,9 +250,17 @@ def main():
     s.add_argument("--command", required=True)
     s.add_argument("--title", required=True)
     s.add_argument("--out", required=True)
+    r = sub.add_parser("apitrace")
+    r.add_argument("--trace", required=True)
+    r.add_argument("--command", required=True)
+    r.add_argument("--out", required=True)
     a = ap.parse_args()
-    text = (traffic_summary(a.fetch, a.write, a.mfma, a.command) if a.what == "traffic"
-            else stats_summary(a.stats, a.command, a.title))
+    if a.what == "traffic":
+        text = traffic_summary(a.fetch, a.write, a.mfma, a.command)
+    elif a.what == "apitrace":
+        text = apitrace_summary(a.trace, a.command)
+    else:
+        text = stats_summary(a.stats, a.command, a.title)
     with open(a.out, "w") as fh:
         fh.write(text)
     print(text)
