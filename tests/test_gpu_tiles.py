@@ -1,7 +1,7 @@
 """Every grouped-GEMM tile shape against the oracle.
 
 The host picks a tile shape from m, k, n and num_local; RD_FWD_TILE and
-RD_TRANS_TILE force one (0..16, read at each call).  Each shape runs the
+RD_TRANS_TILE force one (0..17, read at each call).  Each shape runs the
 three GEMMs on one ragged case (groups against every tile edge, an empty
 group, a window and a limit with NaN rows past it) and must meet the same
 bar as the default choice: float32 output within the GEMM tolerance of the
