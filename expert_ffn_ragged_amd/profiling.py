@@ -217,6 +217,45 @@ def apitrace_summary(trace_dir, command):
     return "\n".join(lines) + "\n"
 
 
+# per-instance counters (one instance per CU) reported as a fraction of the kernel's cycles
+PER_CU = ("TCP_PENDING_STALL_CYCLES", "TCP_UTCL1_STALL_INFLIGHT_MAX", "TA_TA_BUSY", "TA_ADDR_STALLED_BY_TC_CYCLES",
+          "TD_TD_BUSY", "TD_TC_STALL")
+CUS = 256
+
+
+def loadpath_summary(dirs, command):
+    """Load-path counters of the step's kernels: per-CU busy / stall fractions (counter summed over the
+    256 CUs / (GRBM_GUI_ACTIVE / 8 XCDs x 256)), the mean L1 -> L2 read latency
+    (TCP_TCC_READ_REQ_LATENCY / (TCC_HIT + TCC_MISS)) and the L2 hit rate."""
+    means = {}
+    for d in dirs:
+        m, _ = counter_means(d)
+        for (name, ctr), (val, _n) in m.items():
+            means.setdefault(name, {}).setdefault(ctr, []).append(val)
+    lines = ["# Load-path counters: MoE up-projection fwd+bwd step (m8192 k4096 n2048 g64 Zipf 1.1), MI355X", "",
+             "Commands (run from the repository root on the GPU box with `TMPDIR=/tmp` exported; one counter set "
+             "per run):", "", "```", command, "```", "",
+             f"source digest: {source_digest()}", "",
+             "Per-CU fractions are the counter summed over the 256 CUs divided by the kernel's cycles "
+             "(GRBM_GUI_ACTIVE / 8 XCDs) x 256. Read latency is TCP_TCC_READ_REQ_LATENCY / (TCC_HIT + TCC_MISS), "
+             "in cycles per L1 -> L2 read request.", "",
+             "| op | kernel | " + " | ".join(PER_CU) + " | read latency (cycles) | L2 hit rate |",
+             "|---|---|" + "---|" * (len(PER_CU) + 2)]
+    for name, ctrs in sorted(means.items(), key=lambda kv: str(op_of(kv[0]))):
+        if op_of(name) is None or "GRBM_GUI_ACTIVE" not in ctrs:
+            continue
+        gui = sum(ctrs["GRBM_GUI_ACTIVE"]) / len(ctrs["GRBM_GUI_ACTIVE"]) / XCDS
+
+        def frac(c):
+            return f"{ctrs[c][0] / (gui * CUS):.2f}" if c in ctrs and gui else "-"
+
+        req = (ctrs.get("TCC_HIT", [0])[0] + ctrs.get("TCC_MISS", [0])[0])
+        lat = f"{ctrs['TCP_TCC_READ_REQ_LATENCY'][0] / req:.0f}" if req and "TCP_TCC_READ_REQ_LATENCY" in ctrs else "-"
+        hit = f"{ctrs['TCC_HIT'][0] / req:.2f}" if req and "TCC_HIT" in ctrs else "-"
+        lines.append(f"| {op_of(name)} | `{name}` | " + " | ".join(frac(c) for c in PER_CU) + f" | {lat} | {hit} |")
+    return "\n".join(lines) + "\n"
+
+
 def load_traffic(path):
     """{op: traffic bytes per launch} from a traffic summary whose digest matches the sources, else {}."""
     if not os.path.exists(path):
@@ -250,6 +289,10 @@ def main():
     s.add_argument("--command", required=True)
     s.add_argument("--title", required=True)
     s.add_argument("--out", required=True)
+    lp = sub.add_parser("loadpath")
+    lp.add_argument("--dirs", nargs="+", required=True)
+    lp.add_argument("--command", required=True)
+    lp.add_argument("--out", required=True)
     r = sub.add_parser("apitrace")
     r.add_argument("--trace", required=True)
     r.add_argument("--command", required=True)
@@ -257,6 +300,8 @@ def main():
     a = ap.parse_args()
     if a.what == "traffic":
         text = traffic_summary(a.fetch, a.write, a.mfma, a.command)
+    elif a.what == "loadpath":
+        text = loadpath_summary(a.dirs, a.command)
     elif a.what == "apitrace":
         text = apitrace_summary(a.trace, a.command)
     else:
