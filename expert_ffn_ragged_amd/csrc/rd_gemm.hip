@@ -495,6 +495,12 @@ __device__ __forceinline__ void store_block(const f32x16_t& acc, void* out, bool
 // bank slots).
 constexpr int kStagePitch = 36;
 constexpr int kStageFloats = 16 * kStagePitch;  // per wave
+// bf16 staging of a block half: rows of 40 halves (80 bytes: rows r and r + 4
+// of one MFMA-layout write fall 16 banks apart), blocks 1344 bytes apart (the
+// two blocks of a read-back pair start 16 banks apart); fits in kStageFloats.
+constexpr int kStagePitchH = 40;
+constexpr int kStageHalves = 16 * kStagePitchH + 32;
+static_assert(kStageHalves * 2 <= kStageFloats * 4, "bf16 staging fits in the float32 staging area");
 
 // Store a wave's (MI*32) x (NI*32) accumulator block at out[r0.., c0..]
 // (row pitch ld elements, rows < rlim, columns < clim).  Each 32 x 32 block
@@ -533,7 +539,10 @@ __device__ __forceinline__ void store16(V v, void* p) {
 // 4 (l % 8) .. +3 of one block; bf16 (blocks staged in pairs) lane l takes
 // row l / 8, block (l / 4) % 2 of the pair, floats 8 (l % 4) .. +7.  NT marks
 // the stores non-temporal.
-template <int MI, int NI, int NB = NI, int B0 = 0, int NBLK = NI, bool NT = false>
+// S16: bf16 results are rounded before staging (the same RNE per element) and
+// staged as bf16, halving the staging traffic (used by trans_ragged_dot, whose
+// dW tiles dominate its time; the register-heavy fused-GLU tiles would spill).
+template <int MI, int NI, int NB = NI, int B0 = 0, int NBLK = NI, bool NT = false, bool S16 = false>
 __device__ __forceinline__ void store_wave_tile(const f32x16_t (&acc)[MI][NI], void* out, bool f32, long long ld,
                                                 int r0, int rlim, int c0, int clim, float* stage) {
   static_assert(NBLK % NB == 0 && B0 + NBLK <= NI, "blocks staged together must divide the stored range");
@@ -545,12 +554,22 @@ __device__ __forceinline__ void store_wave_tile(const f32x16_t (&acc)[MI][NI], v
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int n0 = 0; n0 < NBLK; n0 += NB) {
+      if (f32 || !S16) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int v = 8 * h; v < 8 * h + 8; ++v)
-          stage[b * kStageFloats + (8 * (v >> 2) - 16 * h + 4 * (l >> 5) + (v & 3)) * kStagePitch + (l & 31)] =
-              acc[mi][B0 + n0 + b][v];
+          for (int v = 8 * h; v < 8 * h + 8; ++v)
+            stage[b * kStageFloats + (8 * (v >> 2) - 16 * h + 4 * (l >> 5) + (v & 3)) * kStagePitch + (l & 31)] =
+                acc[mi][B0 + n0 + b][v];
+      } else {
+        uint16_t* st = reinterpret_cast<uint16_t*>(stage);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int v = 8 * h; v < 8 * h + 8; ++v)
+            st[b * kStageHalves + (8 * (v >> 2) - 16 * h + 4 * (l >> 5) + (v & 3)) * kStagePitchH + (l & 31)] =
+                static_cast<uint16_t>(f32_to_bf16(acc[mi][B0 + n0 + b][v]));
+      }
       if (f32) {
         const int cc = (l & 7) * 4;
 #pragma unroll
@@ -573,15 +592,19 @@ __device__ __forceinline__ void store_wave_tile(const f32x16_t (&acc)[MI][NI], v
 #pragma unroll
           for (int q = 0; q < 16 / (PAIR == 2 ? 8 : 16); ++q) {
             const int row = rows_per * q + rw, b = bp + sub;
-            const float* src = stage + b * kStageFloats + row * kStagePitch + cc;
-            const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(src);
-            const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(src + 4);
             const int grow = r0 + mi * 32 + 16 * h + row, gcol = c0 + (n0 + b) * 32 + cc;
-            if (grow < rlim && gcol < clim) {
-              const u32x4_t v = {pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
-                                 pack_bf16x2(hi[2], hi[3])};
-              store16<NT>(v, static_cast<uint16_t*>(out) + grow * ld + gcol);
+            u32x4_t v;
+            if constexpr (S16) {
+              v = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(stage) + b * kStageHalves +
+                                                    row * kStagePitchH + cc);
+            } else {
+              const float* src = stage + b * kStageFloats + row * kStagePitch + cc;
+              const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(src);
+              const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(src + 4);
+              v = u32x4_t{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
+                          pack_bf16x2(hi[2], hi[3])};
             }
+            if (grow < rlim && gcol < clim) store16<NT>(v, static_cast<uint16_t*>(out) + grow * ld + gcol);
           }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -1174,7 +1197,8 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
     if constexpr (MODE == kFwdGLU)
       store_glu_tile<MI, NI, EPI_H, EPI_H, kNtStores>(acc, p.out, p.out2, p.n, r0, rlim, c0, stage);
     else
-      store_wave_tile<MI, NI, EPI, 0, NI, kNtStores>(acc, out, p.out_f32, p.n, r0, rlim, c0, p.n, stage);
+      store_wave_tile<MI, NI, EPI, 0, NI, kNtStores, is_trans(MODE)>(acc, out, p.out_f32, p.n, r0, rlim, c0, p.n,
+                                                                     stage);
   }
   if constexpr (!is_trans(MODE)) zero_outside_window<NT>(p.out, p.n, p.out_f32 != 0, win);
   if constexpr (MODE == kFwdGLU)
