@@ -523,6 +523,13 @@ constexpr int epilogue_batch(int NI, int elems, int NW) {
     if (NI % nb == 0 && NW * nb * kStageFloats * 2 <= elems) best = nb;
   return best;
 }
+// The same for bf16 staging (blocks of kStageHalves 16-bit elements).
+constexpr int epilogue_batch16(int NI, int elems, int NW) {
+  int best = 0;
+  for (int nb = 1; nb <= NI; ++nb)
+    if (NI % nb == 0 && NW * nb * kStageHalves <= elems) best = nb;
+  return best;
+}
 
 // One 16-byte store, non-temporal (write-once data) when NT.
 template <bool NT, class V>
@@ -540,75 +547,97 @@ __device__ __forceinline__ void store16(V v, void* p) {
 // row l / 8, block (l / 4) % 2 of the pair, floats 8 (l % 4) .. +7.  NT marks
 // the stores non-temporal.
 // S16: bf16 results are rounded before staging (the same RNE per element) and
-// staged as bf16, halving the staging traffic (used by trans_ragged_dot, whose
-// dW tiles dominate its time; the register-heavy fused-GLU tiles would spill).
-template <int MI, int NI, int NB = NI, int B0 = 0, int NBLK = NI, bool NT = false, bool S16 = false>
+// staged as bf16, NB16 blocks at a time: half the staging traffic and, with
+// the smaller blocks, fewer LDS round trips (used by trans_ragged_dot, whose
+// dW tiles dominate its time; the register-heavy fused-GLU tiles would
+// spill).  float32 results, and every result without S16, are staged as
+// float32, NB blocks at a time.
+template <int MI, int NI, int NB = NI, int B0 = 0, int NBLK = NI, bool NT = false, bool S16 = false, int NB16 = NB>
 __device__ __forceinline__ void store_wave_tile(const f32x16_t (&acc)[MI][NI], void* out, bool f32, long long ld,
                                                 int r0, int rlim, int c0, int clim, float* stage) {
-  static_assert(NBLK % NB == 0 && B0 + NBLK <= NI, "blocks staged together must divide the stored range");
+  static_assert(NBLK % NB == 0 && NBLK % NB16 == 0 && B0 + NBLK <= NI, "staged blocks must divide the range");
   const int l = threadIdx.x & 63;
   const int rr = l >> 3;
+  // staging row of MFMA-layout value v of half h
+  auto srow = [&](int v, int h) { return 8 * (v >> 2) - 16 * h + 4 * (l >> 5) + (v & 3); };
+  if (S16 && !f32) {
+    uint16_t* st = reinterpret_cast<uint16_t*>(stage);
+    constexpr int PAIR = NB16 % 2 == 0 ? 2 : 1;
+    const int cc = (l & 3) * 8;
+    const int sub = PAIR == 2 ? (l >> 2) & 1 : 0;
+    const int rows_per = PAIR == 2 ? 8 : 16;
+    const int rw = PAIR == 2 ? rr : (l >> 2);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int n0 = 0; n0 < NBLK; n0 += NB16) {
+#pragma unroll
+          for (int b = 0; b < NB16; ++b)
+#pragma unroll
+            for (int v = 8 * h; v < 8 * h + 8; ++v)
+              st[b * kStageHalves + srow(v, h) * kStagePitchH + (l & 31)] =
+                  static_cast<uint16_t>(f32_to_bf16(acc[mi][B0 + n0 + b][v]));
+#pragma unroll
+          for (int bp = 0; bp < NB16; bp += PAIR)
+#pragma unroll
+            for (int q = 0; q < 16 / rows_per; ++q) {
+              const int row = rows_per * q + rw, b = bp + sub;
+              const int grow = r0 + mi * 32 + 16 * h + row, gcol = c0 + (n0 + b) * 32 + cc;
+              const u32x4_t v = *reinterpret_cast<const u32x4_t*>(st + b * kStageHalves + row * kStagePitchH + cc);
+              if (grow < rlim && gcol < clim) store16<NT>(v, static_cast<uint16_t*>(out) + grow * ld + gcol);
+            }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    return;
+  }
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int n0 = 0; n0 < NBLK; n0 += NB) {
-      if (f32 || !S16) {
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
           for (int v = 8 * h; v < 8 * h + 8; ++v)
-            stage[b * kStageFloats + (8 * (v >> 2) - 16 * h + 4 * (l >> 5) + (v & 3)) * kStagePitch + (l & 31)] =
-                acc[mi][B0 + n0 + b][v];
-      } else {
-        uint16_t* st = reinterpret_cast<uint16_t*>(stage);
+            stage[b * kStageFloats + srow(v, h) * kStagePitch + (l & 31)] = acc[mi][B0 + n0 + b][v];
+        if (f32) {
+          const int cc = (l & 7) * 4;
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
+          for (int b = 0; b < NB; ++b)
 #pragma unroll
-          for (int v = 8 * h; v < 8 * h + 8; ++v)
-            st[b * kStageHalves + (8 * (v >> 2) - 16 * h + 4 * (l >> 5) + (v & 3)) * kStagePitchH + (l & 31)] =
-                static_cast<uint16_t>(f32_to_bf16(acc[mi][B0 + n0 + b][v]));
-      }
-      if (f32) {
-        const int cc = (l & 7) * 4;
+            for (int q = 0; q < 2; ++q) {
+              const int row = 8 * q + rr;
+              const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stage + b * kStageFloats + row * kStagePitch + cc);
+              const int grow = r0 + mi * 32 + 16 * h + row, gcol = c0 + (n0 + b) * 32 + cc;
+              if (grow < rlim && gcol < clim) store16<NT>(v, static_cast<float*>(out) + grow * ld + gcol);
+            }
+        } else {
+          const int cc = (l & 3) * 8;
+          constexpr int PAIR = NB % 2 == 0 ? 2 : 1;
+          const int sub = PAIR == 2 ? (l >> 2) & 1 : 0;
+          const int rows_per = PAIR == 2 ? 8 : 16;  // rows one instruction covers
+          const int rw = PAIR == 2 ? rr : (l >> 2);
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
+          for (int bp = 0; bp < NB; bp += PAIR)
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int row = 8 * q + rr;
-            const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stage + b * kStageFloats + row * kStagePitch + cc);
-            const int grow = r0 + mi * 32 + 16 * h + row, gcol = c0 + (n0 + b) * 32 + cc;
-            if (grow < rlim && gcol < clim) store16<NT>(v, static_cast<float*>(out) + grow * ld + gcol);
-          }
-      } else {
-        const int cc = (l & 3) * 8;
-        constexpr int PAIR = NB % 2 == 0 ? 2 : 1;
-        const int sub = PAIR == 2 ? (l >> 2) & 1 : 0;
-        const int rows_per = PAIR == 2 ? 8 : 16;  // rows one instruction covers
-        const int rw = PAIR == 2 ? rr : (l >> 2);
-#pragma unroll
-        for (int bp = 0; bp < NB; bp += PAIR)
-#pragma unroll
-          for (int q = 0; q < 16 / (PAIR == 2 ? 8 : 16); ++q) {
-            const int row = rows_per * q + rw, b = bp + sub;
-            const int grow = r0 + mi * 32 + 16 * h + row, gcol = c0 + (n0 + b) * 32 + cc;
-            u32x4_t v;
-            if constexpr (S16) {
-              v = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(stage) + b * kStageHalves +
-                                                    row * kStagePitchH + cc);
-            } else {
+            for (int q = 0; q < 16 / rows_per; ++q) {
+              const int row = rows_per * q + rw, b = bp + sub;
               const float* src = stage + b * kStageFloats + row * kStagePitch + cc;
               const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(src);
               const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(src + 4);
-              v = u32x4_t{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
-                          pack_bf16x2(hi[2], hi[3])};
+              const int grow = r0 + mi * 32 + 16 * h + row, gcol = c0 + (n0 + b) * 32 + cc;
+              if (grow < rlim && gcol < clim) {
+                const u32x4_t v = {pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
+                                   pack_bf16x2(hi[2], hi[3])};
+                store16<NT>(v, static_cast<uint16_t*>(out) + grow * ld + gcol);
+              }
             }
-            if (grow < rlim && gcol < clim) store16<NT>(v, static_cast<uint16_t*>(out) + grow * ld + gcol);
-          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
 }
 
 // Zeros for a wave's block (a local group with no rows gets an all +0 dW).
@@ -1069,6 +1098,13 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
   static_assert(MI * 32 == WM && NI * 32 == WN, "wave blocks are whole 32 x 32 MFMA blocks");
   constexpr int A_EL = BM * KS, B_EL = BN * KS, ST = A_EL + B_EL;
   constexpr int EPI = epilogue_batch(NI, ST, NW);
+  // trans_ragged_dot stages bf16 results as bf16, EPI16 blocks at a time; a
+  // wave's staging area covers either layout
+  constexpr int EPI16 = is_trans(MODE) ? epilogue_batch16(NI, ST, NW) : EPI;
+  constexpr int STAGE_HALVES = is_trans(MODE) && EPI16 * kStageHalves > 2 * EPI * kStageFloats
+                                   ? EPI16 * kStageHalves
+                                   : 2 * EPI * kStageFloats;  // per wave
+  static_assert(NW * STAGE_HALVES <= ST, "epilogue staging must fit in one ring slot");
   static_assert(EPI >= 1 && NW * EPI * kStageFloats * 2 <= ST, "epilogue staging must fit in one ring slot");
   // the fused GLU tile: BN weight columns are BN/2 gate + BN/2 up, giving BN/2 output columns
   constexpr int TN = MODE == kFwdGLU ? BN / 2 : BN;
@@ -1193,12 +1229,12 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();  // every wave is done with the last step's slot
     __builtin_amdgcn_sched_barrier(0);
-    float* stage = reinterpret_cast<float*>(s_tiles + ((g + S - 1) % S) * ST) + wave * EPI * kStageFloats;
+    float* stage = reinterpret_cast<float*>(s_tiles + ((g + S - 1) % S) * ST + wave * STAGE_HALVES);
     if constexpr (MODE == kFwdGLU)
       store_glu_tile<MI, NI, EPI_H, EPI_H, kNtStores>(acc, p.out, p.out2, p.n, r0, rlim, c0, stage);
     else
-      store_wave_tile<MI, NI, EPI, 0, NI, kNtStores, is_trans(MODE)>(acc, out, p.out_f32, p.n, r0, rlim, c0, p.n,
-                                                                     stage);
+      store_wave_tile<MI, NI, EPI, 0, NI, kNtStores, is_trans(MODE), EPI16>(acc, out, p.out_f32, p.n, r0, rlim, c0,
+                                                                            p.n, stage);
   }
   if constexpr (!is_trans(MODE)) zero_outside_window<NT>(p.out, p.n, p.out_f32 != 0, win);
   if constexpr (MODE == kFwdGLU)
