@@ -9,7 +9,7 @@
 // free.  Rows at or past the limit are neither read nor written.
 //
 // One wave64 owns a row: lane l handles the 16-byte chunks l, l + 64, ... of
-// it (128-bit non-temporal loads of g and y and stores of the gradient, four
+// it (128-bit non-temporal loads of g and y and stores of the gradient, eight
 // chunks in flight per lane), keeps its part of the dot in float32, and the
 // wave adds the 64 parts in a fixed butterfly order.  A row's dot is therefore
 // produced by exactly one wave: no partial sums cross workgroups, no atomics,
@@ -21,7 +21,7 @@
 namespace rd {
 namespace {
 
-constexpr int kUnroll = 4;  // 16-byte chunks per lane in flight
+constexpr int kUnroll = 8;  // 16-byte chunks per lane in flight (all of a 4096-wide row: 558 -> 545 us)
 
 typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
 
