@@ -1,21 +1,22 @@
 """Benchmark of the ragged-dot hot path on one MI355X.
 
-One step = the MoE up-projection layer (2048 tokens x top-4 = 8192 rows, 64
-experts with Zipf(1.1) sizes, k = 4096, fused wi n = 2048) forward and
-backward, through every kernel of the path:
+Headline step: the MoE backward of a down-projection, the one shape of the
+path that sits at the MFMA ridge (2 x 274.9 GFLOP on 1.7 GB): 32768 rows,
+64 experts with Zipf(1.1) sizes (4 of them empty), w [64, 1024, 4096] bf16:
 
-    fused  = ragged_dot(x, w, gs)                     [8192, 2048] bf16
-    act    = glu_fwd(fused)                           [8192, 1024]
-    dfused = glu_bwd(fused, d_act)                    [8192, 2048]
-    dx     = ragged_dot(dfused, w, gs, trans_rhs)     [8192, 4096]
-    dw     = trans_ragged_dot(x, dfused, gs)          [64, 4096, 2048] bf16
+    dx = ragged_dot(dy [32768, 4096], w, gs, trans_rhs)   [32768, 1024] bf16
+    dW = trans_ragged_dot(x [32768, 1024], dy, gs)         [64, 1024, 4096] bf16
 
-``value`` is the GEMM work on valid rows (3 x 2 * sum(gs) * k * n FLOP) per
-second of step time, the steps launched back to back with HIP events only
-around the whole timed run.  Inputs are synthetic, seeded and resident in HBM
-before timing.  Every kernel is also timed on its own, in a separate loop
-with HIP events around each launch on the stream it runs on; the slowest one
-is reported against its roofline.
+``value`` is the GEMM work on valid rows (2 x 2 * sum(gs) * 1024 * 4096
+FLOP) per second of step time, cold: L2 and the 256 MB MALL are flushed
+before every timed step (a 512 MiB write outside the events), inputs
+resident in HBM.  Each step is bracketed by HIP events on the stream the
+kernels run on, with one more event between dx and dW, which gives each
+kernel's time; the slower kernel is reported against its roofline.  The
+same step is also timed warm (steps back to back, events only at the ends).
+The other workloads (up-projection forward+backward, decode, window+limit,
+GLU and unsort over the packed buffer, fp8) are reported under ``extra``.
+Inputs are synthetic and seeded (expert_ffn_ragged_amd/workloads.py).
 """
 
 import argparse
@@ -38,11 +39,14 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
-    ap.add_argument("--all", action="store_true", help="also time the backward, window+limit and decode workloads")
-    ap.add_argument("--cold", action="store_true",
-                    help="flush L2 and the MALL (a 512 MiB write) before every timed step, outside the events")
+    ap.add_argument("--all", action="store_true",
+                    help="also time the window+limit, packed-buffer GLU and unsort, fp8 and MoE MLP workloads")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="only the headline step (for profiler runs), no extra workloads")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every tile shape of every grouped GEMM on the workloads and print the table")
     ap.add_argument("--copy-calib", action="store_true",
                     help="first copy 256 MiB device-to-device three times (reference kernel for HBM counters)")
     ap.add_argument("--api-region", action="store_true",
@@ -165,13 +169,53 @@ def upproj(steps, warmup):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "upproj_fwd_bwd_traffic.md")
+BACKWARD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "backward_m32768_traffic.md")
 
 
-def measured_traffic():
-    """HBM bytes per launch from the committed counter summary, while the kernels are unchanged."""
+def measured_traffic(path=TRAFFIC_FILE):
+    """HBM bytes per launch from a committed counter summary, while the kernels are unchanged."""
     from expert_ffn_ragged_amd import profiling
 
-    return profiling.load_traffic(TRAFFIC_FILE)
+    return profiling.load_traffic(path)
+
+
+BACKWARD_WORKLOAD = ("moe backward m32768: dx = ragged_dot(dy[32768,4096], w[64,1024,4096], trans_rhs) + "
+                     "dW = trans_ragged_dot(x[32768,1024], dy) bf16, g64 zipf1.1, 4 empty groups")
+
+
+def backward(steps, warmup):
+    """The headline step, cold (caches flushed before each step) and warm."""
+    import torch
+
+    from expert_ffn_ragged_amd import rd, workloads
+
+    d = workloads.make(3, "cuda")
+    x, w, dy, gs = d["x"], d["w"], d["dy"], d["gs"]
+    m, k, n = d["m"], d["k"], d["n"]  # x [m, k], dy [m, n], w [G, k, n] (k = n_out of dx)
+    rows = int(d["gs_host"].sum())
+    nonempty = int((d["gs_host"] > 0).sum())
+    dx = torch.empty((m, k), dtype=torch.bfloat16, device="cuda")
+    dw = torch.empty((d["G"], k, n), dtype=torch.bfloat16, device="cuda")
+    ops = [
+        ("ragged_dot_trans_rhs", lambda: rd.ragged_dot(dy, w, gs, trans_rhs=True, out=dx)),
+        ("trans_ragged_dot", lambda: rd.trans_ragged_dot(x, dy, gs, out=dw)),
+    ]
+    COLD["on"] = True
+    wall, cold_ms, cold_per = timed_ops(ops, steps, warmup)
+    cold_pct = {name: PERCENTILES[name] for name, _ in ops}
+    COLD["on"] = False
+    _, _, warm_per = timed_ops(ops, steps, warmup)
+    warm_step = step_timed(ops, steps, warmup) / steps
+    flop = 2.0 * rows * k * n
+    b = 2  # bf16 bytes
+    # algorithmic bytes: every operand read once (the weights of non-empty experts only), every result
+    # written once (dW of an empty expert is written as zeros)
+    nbytes = {"ragged_dot_trans_rhs": rows * n * b + nonempty * k * n * b + rows * k * b,
+              "trans_ragged_dot": rows * k * b + rows * n * b + d["G"] * k * n * b}
+    return dict(rows=rows, m=m, k=k, n=n, G=d["G"], wall=wall, cold_ms=cold_ms / steps, cold_per=cold_per,
+                cold_pct=cold_pct, warm_per=warm_per, warm_step=warm_step, bytes=nbytes,
+                flops={"ragged_dot_trans_rhs": flop, "trans_ragged_dot": flop}, step_flop=2 * flop,
+                tensors=(x, w, dy, d["gs_host"]))
 
 
 def roofline(name, ms, nbytes, flop, traffic=None):
@@ -190,19 +234,31 @@ def roofline(name, ms, nbytes, flop, traffic=None):
             "algorithmic_bytes": int(nbytes), "flop": flop}
 
 
-def extra_workloads(steps):
-    """Single-op timings of the other workloads (reported beside the headline)."""
+def extra_workloads(steps, warmup):
+    """The up-projection forward+backward step and the decode GEMM (reported beside the headline)."""
     import torch
 
     from expert_ffn_ragged_amd import rd, workloads
 
     out = {}
+    r = upproj(steps, warmup)
+    traffic = measured_traffic()
+    step_ms = r["step_ms"] / steps
+    out["upproj_fwd_bwd_m8192_k4096_n2048_g64"] = {
+        "ms_per_step": round(step_ms, 4), "TFLOP/s": round(r["step_flop"] / step_ms / 1e9, 1),
+        "mfma_frac": round(r["step_flop"] / step_ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "timing": "warm; steps back to back, per-kernel times from a loop with events around each launch",
+        "per_kernel": {name: dict(roofline(name, ms, r["bytes"][name], r["flops"][name], traffic.get(name)),
+                                  p10_p50_p90_ms=PERCENTILES.get(name))
+                       for name, ms in r["per_op"].items()}}
+    del r
+    torch.cuda.empty_cache()
     d = workloads.make(5, "cuda", parts=("x", "w"))
     o = torch.empty((d["m"], d["n"]), dtype=torch.bfloat16, device="cuda")
     wsb = rd.library().rd_forward_workspace_size(d["m"], d["k"], d["n"], d["G"], 0)
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
     _, _, per = timed_ops([("decode", lambda: rd.ragged_dot(d["x"], d["w"], d["gs"], out=o, workspace=ws))],
-                          steps, 3)
+                          steps, warmup)
     nz = d["gs_host"] > 0
     rows = int(d["gs_host"].sum())
     # algorithmic bytes: x rows, the weights of non-empty experts, the output
@@ -232,8 +288,6 @@ def extra_all(steps):
     dw = torch.empty((d["G"], k, n), dtype=torch.bfloat16, device="cuda")
     dw32 = torch.empty((d["G"], k, n), dtype=torch.float32, device="cuda")
     _, _, per = timed_ops([
-        ("dx", lambda: rd.ragged_dot(d["dy"], d["w"], d["gs"], trans_rhs=True, out=dx)),
-        ("dw_bf16", lambda: rd.trans_ragged_dot(d["x"], d["dy"], d["gs"], out=dw)),
         ("dw_f32", lambda: rd.trans_ragged_dot(d["x"], d["dy"], d["gs"], out=dw32)),
     ], steps, 3)
     # context: the vendor library's dense bf16 GEMM of the same flops (dy [m, n] times one expert's
@@ -426,35 +480,51 @@ def api_region(iters=5):
     print(json.dumps({"api_region": "done", "iters": iters}), flush=True)
 
 
-def cpu_baseline(x, w, dy, gs_host, budget_s=12.0):
-    """The CPU oracle, as it stands, on a bounded sample of the timed workload.
+def cpu_info():
+    """CPU model (from /proc/cpuinfo), the cores this process may run on, and numpy's BLAS threads."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    affinity = len(os.sched_getaffinity(0))
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
 
-    Runs the oracle's ragged_dot, trans_rhs ragged_dot and trans_ragged_dot
-    expert by expert on the same tensors the GPU just processed (copied to the
-    host one expert at a time) until about ``budget_s`` seconds are spent.
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: numpy's BLAS defaults to the affinity set
+        blas = affinity
+    return model, affinity, int(blas)
+
+
+def cpu_baseline(x, w, dy, gs_host, budget_s=15.0):
+    """The CPU oracle, as it stands, on a bounded sample of the headline workload.
+
+    Runs the oracle's trans_rhs ragged_dot (dx) and trans_ragged_dot (dW) expert by expert, largest
+    expert first, on the same tensors the GPU just processed (copied to the host one expert at a
+    time), until about ``budget_s`` seconds are spent.
     """
     import numpy as np
 
     import oracle
     from expert_ffn_ragged_amd.workloads import bits
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # threadpoolctl missing: report the affinity set numpy's BLAS defaults to
-        cores = len(os.sched_getaffinity(0))
+    model, affinity, blas = cpu_info()
     lb = np.concatenate([[0], np.cumsum(gs_host)])
     k, n = w.shape[1], w.shape[2]
     spent, rows, experts = 0.0, 0, 0
-    for j in range(len(gs_host)):
+    for j in np.argsort(-gs_host, kind="stable"):
         r0, r1 = int(lb[j]), int(lb[j + 1])
         if r1 == r0:
             continue
         xb, dyb, wb = bits(x[r0:r1]), bits(dy[r0:r1]), bits(w[j:j + 1])
         one = np.array([r1 - r0], dtype=np.int32)
         t0 = time.perf_counter()
-        oracle.ragged_dot(xb, wb, one)
         oracle.ragged_dot(dyb, wb, one, trans_rhs=True)
         oracle.trans_ragged_dot(xb, dyb, one)
         spent += time.perf_counter() - t0
@@ -462,10 +532,60 @@ def cpu_baseline(x, w, dy, gs_host, budget_s=12.0):
         experts += 1
         if spent >= budget_s:
             break
-    flop = 3 * 2.0 * rows * k * n
-    return {"value": round(flop / spent / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"oracle ragged_dot + trans_rhs ragged_dot + trans_ragged_dot (float64) on the timed "
-                      f"up-projection tensors, {experts} of 64 experts ({rows} of 8192 rows), {spent:.1f} s"}
+    flop = 2 * 2.0 * rows * k * n
+    nz = int((gs_host > 0).sum())
+    return {"value": round(flop / spent / 1e12, 6), "unit": "TFLOP/s", "cores": blas, "kind": "oracle",
+            "sample": f"oracle trans_rhs ragged_dot (dx) + trans_ragged_dot (dW), float64, on the timed backward "
+                      f"tensors, {experts} of {nz} non-empty experts largest first ({rows} of {int(gs_host.sum())} "
+                      f"rows), {spent:.1f} s",
+            "cpu_model": model, "affinity_cores": affinity, "blas_threads": blas}
+
+
+def sweep(steps):
+    """Every tile shape of every grouped GEMM on the workloads: one JSON line per (op, tile) with its mean
+    time, then one summary line per op with the built-in choice and the fastest shape."""
+    import torch
+
+    from expert_ffn_ragged_amd import rd, workloads
+
+    cases = []
+    d2 = workloads.make(2, "cuda", parts=("x", "w", "dy"))
+    m2, k2, n2 = d2["m"], d2["k"], d2["n"]
+    o2 = torch.empty((m2, n2), dtype=torch.bfloat16, device="cuda")
+    dx2 = torch.empty((m2, k2), dtype=torch.bfloat16, device="cuda")
+    dw2 = torch.empty((64, k2, n2), dtype=torch.bfloat16, device="cuda")
+    act2 = torch.empty((m2, n2 // 2), dtype=torch.bfloat16, device="cuda")
+    cases += [("upproj_ragged_dot", "fwd", lambda: rd.ragged_dot(d2["x"], d2["w"], d2["gs"], out=o2)),
+              ("upproj_ragged_dot_glu", "fwd", lambda: rd.ragged_dot_glu(d2["x"], d2["w"], d2["gs"], act=act2)),
+              ("upproj_dx_trans_rhs", "fwd",
+               lambda: rd.ragged_dot(d2["dy"], d2["w"], d2["gs"], trans_rhs=True, out=dx2)),
+              ("upproj_dw_trans_ragged_dot", "trans", lambda: rd.trans_ragged_dot(d2["x"], d2["dy"], d2["gs"],
+                                                                                    out=dw2))]
+    d3 = workloads.make(3, "cuda")
+    dx3 = torch.empty((d3["m"], d3["k"]), dtype=torch.bfloat16, device="cuda")
+    dw3 = torch.empty((64, d3["k"], d3["n"]), dtype=torch.bfloat16, device="cuda")
+    cases += [("backward_dx_trans_rhs", "fwd",
+               lambda: rd.ragged_dot(d3["dy"], d3["w"], d3["gs"], trans_rhs=True, out=dx3)),
+              ("backward_dw_trans_ragged_dot", "trans", lambda: rd.trans_ragged_dot(d3["x"], d3["dy"], d3["gs"],
+                                                                                      out=dw3))]
+    d5 = workloads.make(5, "cuda", parts=("x", "w"))
+    o5 = torch.empty((d5["m"], d5["n"]), dtype=torch.bfloat16, device="cuda")
+    cases += [("decode_ragged_dot_tile_path", "fwd", lambda: rd.ragged_dot(d5["x"], d5["w"], d5["gs"], out=o5))]
+    ntile = rd.tile_count()
+    for name, kind, fn in cases:
+        times = {}
+        for tile in [None] + list(range(ntile)):
+            kw = {"fwd_tile" if kind == "fwd" else "trans_tile": tile, "decode": False}
+            with rd.tuning(**kw):
+                _, _, per = timed_ops([(name, fn)], steps, 2)
+            times["default" if tile is None else tile] = per[name]
+            print(json.dumps({"sweep": name, "tile": "default" if tile is None else tile,
+                              "ms": round(per[name], 4)}), flush=True)
+        best = min((t for t in times if t != "default"), key=lambda t: times[t])
+        print(json.dumps({"sweep_summary": name, "default_ms": round(times["default"], 4), "best_tile": best,
+                          "best_ms": round(times[best], 4)}), flush=True)
+    del d2, d3, d5
+    torch.cuda.empty_cache()
 
 
 def main():
@@ -486,7 +606,9 @@ def main():
     if args.api_region:
         api_region()
         return
-    COLD["on"] = args.cold
+    if args.sweep:
+        sweep(max(args.steps, 5))
+        return
     if args.copy_calib:
         a = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
@@ -494,11 +616,11 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         del a, b
-    r = upproj(args.steps, args.warmup)
-    traffic = measured_traffic()
-    ms_step = (r["gpu_ms"] if r["step_ms"] is None else r["step_ms"]) / args.steps
+    r = backward(args.steps, args.warmup)
+    traffic = measured_traffic(BACKWARD_TRAFFIC_FILE)
+    ms_step = r["cold_ms"]
     value = r["step_flop"] / (ms_step * 1e-3) / 1e12
-    dom = max(r["per_op"], key=r["per_op"].get)
+    dom = max(r["cold_per"], key=r["cold_per"].get)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -512,23 +634,27 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "moe up-projection fwd+bwd: m8192 (2048 tok x top4) k4096 n2048 g64 zipf1.1",
-                   "m": r["m"], "k": r["k"], "n": r["n"], "groups": r["G"], "valid_rows": r["rows"],
-                   "parallelism": "none (1 GPU)"},
+        "config": {"workload": BACKWARD_WORKLOAD, "m": r["m"], "k": r["k"], "n": r["n"], "groups": r["G"],
+                   "valid_rows": r["rows"], "parallelism": "none (1 GPU)"},
         "pct_bf16_mfma_peak": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
-        "roofline": roofline(dom, r["per_op"][dom], r["bytes"][dom], r["flops"][dom], traffic.get(dom)),
+        "roofline": roofline(dom, r["cold_per"][dom], r["bytes"][dom], r["flops"][dom], traffic.get(dom)),
         "per_kernel": {name: dict(roofline(name, ms, r["bytes"][name], r["flops"][name], traffic.get(name)),
-                                  p10_p50_p90_ms=PERCENTILES.get(name))
-                       for name, ms in r["per_op"].items()},
-        "ms_per_step_with_op_events": round(r["gpu_ms"] / args.steps, 4),
-        "timing": ("cold (L2 and MALL flushed before each step)" if args.cold else
-                   "warm (inputs resident, caches warm); steps timed back to back with events only at the ends, "
-                   "per-kernel times from a separate loop with events around each launch"),
+                                  p10_p50_p90_ms=r["cold_pct"][name])
+                       for name, ms in r["cold_per"].items()},
+        "timing": ("cold: L2 and MALL flushed (512 MiB write) before each step, outside the events; HIP events "
+                   "before dx, between dx and dW and after dW on the stream both run on"),
+        "warm": {"ms_per_step": round(r["warm_step"], 4),
+                 "TFLOP/s": round(r["step_flop"] / r["warm_step"] / 1e9, 1),
+                 "per_kernel_ms": {name: round(ms, 4) for name, ms in r["warm_per"].items()},
+                 "timing": "steps back to back with events only at the ends; per-kernel times from a separate "
+                           "loop with events around each launch"},
     }
-    line["extra"] = extra_workloads(max(args.steps, 10))
-    if args.all:
-        line["extra"].update(extra_all(max(args.steps, 10)))
-    line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(*r["tensors"])
+    backward_tensors = r["tensors"]
+    if not args.headline_only:
+        line["extra"] = extra_workloads(max(args.steps, 10), args.warmup)
+        if args.all:
+            line["extra"].update(extra_all(max(args.steps, 10)))
+    line["cpu_baseline"] = None if (args.no_cpu_baseline or args.headline_only) else cpu_baseline(*backward_tensors)
     print(json.dumps(line), flush=True)
 
 

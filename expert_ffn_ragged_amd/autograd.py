@@ -20,10 +20,14 @@ device-resident ``group_sizes``; nothing is copied to the host, so forward
 and backward can be captured in a HIP graph.
 
 With a ``limit`` (the packed expert buffer's valid rows), rows at or past it
-are neither read nor written by any kernel: those rows of ``out`` and of the
-input gradient are left as allocated (uninitialised) unless ``zero_tail``
-is set, as on the page, where rows left unwritten are never read.
-Gradients come back in the dtype of their input (bf16).
+are neither read nor written by the GEMM and GLU kernels.  Those rows of a
+forward output are left as allocated unless ``zero_tail`` is set (the
+MaxText page's valid-rows commit: nothing downstream consumes them).  The
+gradient of an input there is exactly zero, and that is what comes back: a
+device-side kernel (``rd.zero_rows_from_limit``, limit read on the GPU)
+writes those rows as +0, so no uninitialised memory reaches accumulation,
+clipping or a scatter of the gradient.  Gradients come back in the dtype of
+their input (bf16).
 """
 
 import torch
@@ -51,7 +55,7 @@ class RaggedDot(torch.autograd.Function):
         dx = dw = None
         if ctx.needs_input_grad[0]:
             # d/dx of x @ w is dout @ w^T; with trans_rhs (x @ w^T) it is dout @ w
-            dx = rd.ragged_dot(dout, w, gs, off, lim, trans_rhs=not ctx.trans_rhs)
+            dx = rd.zero_rows_from_limit(rd.ragged_dot(dout, w, gs, off, lim, trans_rhs=not ctx.trans_rhs), lim)
         if ctx.needs_input_grad[1]:
             gl = w.shape[0]
             if ctx.trans_rhs:   # w[j] is [n, k]: dw[j] = dout_j^T x_j
@@ -76,9 +80,9 @@ class TransRaggedDot(torch.autograd.Function):
         dz = dz.to(x.dtype).contiguous()
         dx = dy = None
         if ctx.needs_input_grad[0]:
-            dx = rd.ragged_dot(y, dz, gs, off, lim, trans_rhs=True)   # dx_r = y_r @ dz[j]^T
+            dx = rd.zero_rows_from_limit(rd.ragged_dot(y, dz, gs, off, lim, trans_rhs=True), lim)  # y_r @ dz[j]^T
         if ctx.needs_input_grad[1]:
-            dy = rd.ragged_dot(x, dz, gs, off, lim)                   # dy_r = x_r @ dz[j] (the review's fix)
+            dy = rd.zero_rows_from_limit(rd.ragged_dot(x, dz, gs, off, lim), lim)  # x_r @ dz[j] (the review's fix)
         return (dx, dy) + _none_grads(5)
 
 
@@ -112,8 +116,7 @@ class MoeMLP(torch.autograd.Function):
         d_fused = rd.glu_bwd(fused, d_act, lim)                              # [d_gate | d_up]
         dx = None
         if ctx.needs_input_grad[0]:
-            dx = torch.zeros_like(x) if ctx.zero_tail else None
-            dx = rd.ragged_dot(d_fused, wi, gs, off, lim, trans_rhs=True, out=dx)
+            dx = rd.zero_rows_from_limit(rd.ragged_dot(d_fused, wi, gs, off, lim, trans_rhs=True), lim)
         dwi = rd.trans_ragged_dot(x, d_fused, gs, gl, off, lim, out_dtype=wi.dtype)
         return (dx, dwi, dwo) + _none_grads(4)
 

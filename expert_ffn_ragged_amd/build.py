@@ -29,6 +29,7 @@ SOURCES = [
     ("rd_gemm.hip", []),
     ("rd_glu.hip", ["-ffp-contract=off"]),
     ("rd_unsort.hip", []),
+    ("rd_rows.hip", []),
     ("rd_api.cpp", ["-x", "hip"]),
 ]
 

@@ -301,4 +301,18 @@ int rd_unsort_bwd_rows(const void* g, const void* y, const float* w, const int32
                                     static_cast<hipStream_t>(stream));
 }
 
+int rd_zero_rows_from_limit(void* buf, const int32_t* limit, int64_t rows, int64_t row_bytes, void* stream) {
+  if (rows < 0 || row_bytes <= 0) return RD_EINVAL;
+  if ((row_bytes % 16) != 0) return RD_EUNSUPPORTED;
+  if (rows > 0 && row_bytes > (int64_t(1) << 62) / rows) return RD_EUNSUPPORTED;
+  if (rows == 0 || limit == nullptr) return RD_OK;  // no rows past the limit: nothing to write
+  if (!buf) return RD_EINVAL;
+  if (!aligned16(buf) || (reinterpret_cast<uintptr_t>(limit) & 3u)) return RD_EINVAL;
+  return rd::launch_zero_rows(buf, limit, rows, row_bytes, static_cast<hipStream_t>(stream));
+}
+
+int rd_tune_set(int32_t which, int32_t value) { return rd::tune_set(which, value); }
+
+int rd_tune_tile_count(void) { return rd::tile_count(); }
+
 }  // extern "C"

@@ -32,7 +32,7 @@
 //  * LDS tiles are XOR-swizzled at 16-byte granularity instead of padded;
 //  * tiles are ordered so that consecutive logical tiles land on one XCD,
 //    which keeps a group's weight slab and rows in that XCD's L2.
-#include <cstdlib>
+#include <atomic>
 #include <type_traits>
 
 #include "rd_device.h"
@@ -235,14 +235,14 @@ __device__ __forceinline__ u32x4_t make_rsrc(const void* base, unsigned long lon
 // (lds must be wave-uniform).  Issued as inline assembly so that the
 // compiler does not drain the queue before every later LDS read; the
 // pipeline below waits for these loads explicitly with s_waitcnt vmcnt.
-// M0 holds the LDS base and needs one wait state before the load uses it.
-// M0 is a reserved register (never allocated; the compiler sets it right
-// before each instruction that reads it), so it is not listed as clobbered.
+// M0 holds the LDS base and needs one wait state before the load uses it;
+// it is declared clobbered, so the compiler re-establishes any M0 value of
+// its own after the load.
 __device__ __forceinline__ void dma16(u32x4_t r, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
                : "s"(lds_addr), "v"(voff), "s"(r), "s"(soff)
-               : "memory");
+               : "memory", "m0");
 }
 
 // The same load marked non-temporal, for data read exactly once (the decode
@@ -251,7 +251,7 @@ __device__ __forceinline__ void dma16_nt(u32x4_t r, uint32_t lds_addr, uint32_t 
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
                :
                : "s"(lds_addr), "v"(voff), "s"(r), "s"(soff)
-               : "memory");
+               : "memory", "m0");
 }
 
 // Scalar operands of dma16 are wave-uniform by construction; readfirstlane
@@ -468,25 +468,6 @@ __device__ __forceinline__ void k_loop(OpA& A, OpB& B, int nk, uint16_t* s_tiles
       B.store(sb[cur ^ 1]);
     }
     __syncthreads();
-  }
-}
-
-// Store one 32x32 accumulator block directly.  MFMA 32x32 result layout: lane
-// l, value v holds row 8*(v/4) + 4*(l/32) + v%4, column l%32 of the block.
-__device__ __forceinline__ void store_block(const f32x16_t& acc, void* out, bool f32, long long ld, int r0, int rlim,
-                                            int c0, int clim) {
-  const int l = threadIdx.x & 63;
-  const int c = c0 + (l & 31);
-  if (c >= clim) return;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int r = r0 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
-    if (r < rlim) {
-      if (f32)
-        static_cast<float*>(out)[r * ld + c] = acc[v];
-      else
-        static_cast<uint16_t*>(out)[r * ld + c] = static_cast<uint16_t>(f32_to_bf16(acc[v]));
-    }
   }
 }
 
@@ -1241,6 +1222,221 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
     if (p.out2 != nullptr) zero_outside_window<NT>(p.out2, 2 * p.n, false, win);
 }
 
+// ---------------------------------------------------------------- ping-pong 256 x 256 kernel
+
+// s_waitcnt immediate for "lgkmcnt(0)" leaving vmcnt/expcnt unconstrained.
+constexpr int kLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);
+
+// Fragments of one phase: NSL slices of the 32x32x16 MFMA.
+template <int MI, int NI, int NSL>
+struct PPFrags {
+  bf16x8_t a[NSL][MI], b[NSL][NI];
+};
+
+// 256 x 256 output tiles on eight waves that take turns (ping-pong).  The
+// waves form two groups of four, one wave of each group per SIMD (a
+// workgroup's waves w and w + 4 share a SIMD, measured).  Each KS-deep stage
+// of the buffer-to-LDS ring (whole 128-byte rows of a contraction-contiguous
+// operand at KS = 64) is consumed in two halves, and every half has two
+// phases separated by workgroup barriers: a memory phase (the half's LDS ->
+// register fragment reads) and a compute phase (its MFMAs from registers).
+// Group B runs one phase behind group A, so in every phase one wave per SIMD
+// issues MFMAs back to back while its SIMD partner reads LDS:
+//
+//   phase   0       1       2       3       4    ...
+//   A      M(0a)   C(0a)   M(0b)   C(0b)   M(1a)
+//   B       -      M(0a)   C(0a)   M(0b)   C(0b)
+//
+// Ring discipline (S slots, stage g in slot g % S): stage g's slot is read
+// last in phase 4g + 3, so its refill with stage g + S starts in phase
+// 4g + 4 (group A at the start of M((g+1)a), group B at the start of its
+// compute phase C(gb)); group B's prologue loads one stage more than A's.
+// Stage g + 1 must have landed by phase 4g + 4: each wave waits for its own
+// share before the barrier that opens that phase, and finishes its LDS reads
+// (lgkmcnt 0) before the barrier that closes each memory phase.  Each wave
+// owns a 64 x 128 block (rows 64 (w / 2), columns 128 (w % 2)): group A holds
+// the tile's first 128 rows, so a forward tile with at most 128 valid rows
+// leaves group B's MFMAs and fragment reads out.  A tile's epilogue runs in
+// the wave's next memory phase (staged through a private LDS area), while
+// the other group multiplies.
+template <int MODE, int S, int KS, int MAXL = RD_MAX_GROUPS>
+__global__ __launch_bounds__(512, 1) void grouped_gemm_pp(KArgs p) {
+  constexpr int BM = 256, BN = 256, NW = 8, NT = NW * 64;
+  constexpr int WM = 64, WN = 128, MI = WM / 32, NI = WN / 32;
+  constexpr int HALVES = 2, NSL = KS / 16 / HALVES;  // phases per stage, MFMA slices per phase
+  constexpr int A_EL = BM * KS, B_EL = BN * KS, ST = A_EL + B_EL;
+  constexpr int EPI16 = 2;  // bf16 results: blocks staged per LDS round trip
+  constexpr int STAGE_F = (kStageHalves * EPI16 + 1) / 2 > kStageFloats ? (kStageHalves * EPI16 + 1) / 2
+                                                                         : kStageFloats;  // floats per wave
+  static_assert(STAGE_F % 4 == 0 && NSL >= 1, "staging areas stay 16-byte aligned");
+  constexpr bool kNtStores = true;
+  using Ops = StreamOps<MODE, BM, BN, KS, NW>;
+  using OpA = typename Ops::A;
+  using OpB = typename Ops::B;
+  using Tiles = typename std::conditional<is_trans(MODE), TransTiles, FwdTiles>::type;
+  constexpr int L = OpA::kInstr + OpB::kInstr;  // loads per wave per stage
+  static_assert(S >= 2 && (S - 1) * L <= 63, "ring depth");
+  __shared__ __attribute__((aligned(1024))) uint16_t s_tiles[S * ST];
+  __shared__ __attribute__((aligned(16))) float s_stage[NW * STAGE_F];
+  __shared__ int s_lb[MAXL + 1];
+  __shared__ int s_aux[MAXL + 1];
+  __shared__ long long s_wave[NW];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wave >> 2;
+  const int wm_off = (wave >> 1) * WM, wn_off = (wave & 1) * WN;
+  float* stage = s_stage + wave * STAGE_F;
+  const Window win = build_local_bounds<NT>(p.gs, p.G, p.offp, p.gl, p.limp, p.m, s_lb, s_wave);
+
+  Tiles tl;
+  if constexpr (is_trans(MODE)) {
+    order_groups<NT>(s_lb, p.gl, s_aux);
+    tl.init(p.gl, p.k, p.n, BM, BN);
+  } else {
+    const int total_m = tile_prefix<NT>(s_lb, p.gl, BM, s_aux, s_wave);
+    tl.init(total_m, p.n, BN, p.k);
+  }
+  auto tile_at = [&](long long s, typename Tiles::Tile& t) -> bool {
+    if constexpr (is_trans(MODE))
+      return tl.template get<BM, BN, KS>(s, s_lb, s_aux, t);
+    else
+      return tl.template get<BM, BN, KS>(s, s_lb, s_aux, p.gl, p.k, t);
+  };
+  const uint32_t ring = lds_address(s_tiles);
+  const long long stride = gridDim.x;
+
+  // producer: this wave's share of every stage, walking the tile list ahead of the consumer
+  long long ps = static_cast<long long>(blockIdx.x) - stride;
+  int p_kt = 0, p_nk = 0;
+  bool p_done = false;
+  OpA pa;
+  OpB pb;
+  int issued = 0;
+  auto produce = [&]() {
+    while (!p_done && p_kt >= p_nk) {
+      ps += stride;
+      if (ps >= tl.slots) {
+        p_done = true;
+        break;
+      }
+      typename Tiles::Tile t;
+      if (tile_at(ps, t) && t.nk > 0) {
+        Ops::make(p, t, wave, pa, pb);
+        p_kt = 0;
+        p_nk = t.nk;
+      }
+    }
+    if (p_done) return;
+    const uint32_t slot = ring + 2 * (issued % S) * ST;
+    pa.issue(slot, p_kt, wave);
+    pb.issue(slot + 2 * A_EL, p_kt, wave);
+    ++p_kt;
+    ++issued;
+  };
+  auto barrier = []() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+#pragma unroll
+  for (int i = 0; i < S - 1; ++i) produce();
+  if (grp == 1) produce();                              // group B issues its stage-(S-1) share up front
+  if (issued > 0) wait_ladder<L, S - 1>(issued - 1);  // stage 0 of this wave landed
+  barrier();
+  if (grp == 1) barrier();  // group B runs one phase behind
+
+  int g = 0;  // consumer stage
+  for (long long cs = blockIdx.x; cs < tl.slots; cs += stride) {
+    typename Tiles::Tile t;
+    if (!tile_at(cs, t)) continue;
+    char* out;
+    int r0, rlim, c0;
+    if constexpr (is_trans(MODE)) {
+      out = static_cast<char*>(p.out) + static_cast<long long>(t.j) * p.k * p.n * (p.out_f32 ? 4 : 2);
+      r0 = t.a0 + wm_off;
+      rlim = p.k;
+      c0 = t.c0 + wn_off;
+    } else {
+      out = static_cast<char*>(p.out);
+      r0 = t.row0 + wm_off;
+      rlim = t.row_end;
+      c0 = t.n0 + wn_off;
+    }
+    if (t.nk == 0) {  // a local group with no rows: its dW tile is +0
+      store_wave_zero<MI, NI>(out, p.out_f32, p.n, r0, rlim, c0, p.n);
+      continue;
+    }
+    if (r0 >= rlim) {
+      // this wave's rows lie past the tile's valid rows: only its share of the loads, the waits and
+      // the barriers, so that its SIMD partner multiplies alone
+      for (int kt = 0; kt < t.nk; ++kt) {
+#pragma unroll
+        for (int h = 0; h < HALVES; ++h) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (grp == 0 && h == 0) produce();
+          __builtin_amdgcn_sched_barrier(0);
+          const bool more = issued > g + 1;
+          if (grp == 1 && h == HALVES - 1 && more) wait_ladder<L, S - 1>(issued - 2 - g);
+          barrier();
+          if (grp == 1 && h == HALVES - 1) produce();
+          __builtin_amdgcn_sched_barrier(0);
+          if (grp == 0 && h == HALVES - 1 && more) wait_ladder<L, S - 1>(issued - 2 - g);
+          barrier();
+        }
+        ++g;
+      }
+      continue;
+    }
+    f32x16_t acc[MI][NI];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x16_t{};
+    for (int kt = 0; kt < t.nk; ++kt) {
+      const uint16_t* slot = s_tiles + (g % S) * ST;
+#pragma unroll
+      for (int h = 0; h < HALVES; ++h) {
+        // ---- memory phase of half h of stage g
+        __builtin_amdgcn_sched_barrier(0);
+        if (grp == 0 && h == 0) produce();  // refill the slot stage g - 1 left
+        __builtin_amdgcn_sched_barrier(0);
+        PPFrags<MI, NI, NSL> fr;
+#pragma unroll
+        for (int q = 0; q < NSL; ++q) {
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi) fr.a[q][mi] = OpA::frag(slot, wm_off + mi * 32, h * NSL + q);
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) fr.b[q][ni] = OpB::frag(slot + A_EL, wn_off + ni * 32, h * NSL + q);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(kLgkm0);  // fragments in registers before the slot may be refilled
+        const bool more = issued > g + 1;
+        if (grp == 1 && h == HALVES - 1 && more) wait_ladder<L, S - 1>(issued - 2 - g);  // stage g + 1 landed
+        barrier();
+        // ---- compute phase of half h of stage g
+        if (grp == 1 && h == HALVES - 1) produce();  // refill the slot stage g - 1 left
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < NSL; ++q)
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni)
+              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.a[q][mi], fr.b[q][ni], acc[mi][ni], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (grp == 0 && h == HALVES - 1 && more) wait_ladder<L, S - 1>(issued - 2 - g);
+        barrier();
+      }
+      ++g;
+    }
+    // epilogue: the start of this wave's next memory phase, while the other group multiplies
+    store_wave_tile<MI, NI, 1, 0, NI, kNtStores, true, EPI16>(acc, out, p.out_f32, p.n, r0, rlim, c0, p.n, stage);
+  }
+  if (grp == 0) barrier();  // group A matches group B's leading barrier
+  if constexpr (!is_trans(MODE)) zero_outside_window<NT>(p.out, p.n, p.out_f32 != 0, win);
+}
+
 // ---------------------------------------------------------------- decode: split contraction
 
 // ragged_dot with a few rows per group (decode: ~5 rows per expert) is a
@@ -1494,13 +1690,15 @@ int grid_size(long long work_items, int per_cu) {
 // per MFMA, smaller BM wastes fewer MFMA rows on short groups.
 enum Tile { kT64x128 = 0, kT128x128 = 1, kT128x256 = 2, kT256x256 = 3, kT128x128x2 = 4, kT64x64 = 5, kT256x256k32 = 6,
             kT128x256k32 = 7, kT128x256x2 = 8, kT128x128k32x2 = 9, kT128x128x3 = 10, kT256x128x2 = 11,
-            kT128x256s3x2 = 12, kW256x256 = 13, kW128x256 = 14, kW256x256k64 = 15, kW128x512 = 16, kW128x256k32 = 17, kTileCount };
+            kT128x256s3x2 = 12, kW256x256 = 13, kW128x256 = 14, kW256x256k64 = 15, kW128x512 = 16, kW128x256k32 = 17, kP256x256 = 18, kTileCount };
 
-// RD_FWD_TILE / RD_TRANS_TILE (0..17) force a shape, for tile sweeps.
-int forced_tile(const char* name) {
-  const char* v = getenv(name);
-  if (v == nullptr || *v == 0) return -1;
-  const int t = atoi(v);
+// Tuning overrides set through rd_tune_set (tile sweeps only): a forced
+// forward / trans tile shape (-1: the host heuristic) and the decode path
+// switch (1 on, 0 off).  Plain atomics: a call reads each once.
+std::atomic<int> g_tune[3] = {{-1}, {-1}, {1}};
+
+int forced_tile(int which) {
+  const int t = g_tune[which].load(std::memory_order_relaxed);
   return (t >= 0 && t < kTileCount) ? t : -1;
 }
 
@@ -1516,7 +1714,7 @@ int forced_tile(const char* name) {
 // stores).  Chosen from sweeps of every shape on the up-projection,
 // backward, window+limit and decode workloads.
 int pick_forward_tile(const GemmProblem& p, bool trans_rhs) {
-  const int forced = forced_tile("RD_FWD_TILE");
+  const int forced = forced_tile(RD_TUNE_FWD_TILE);
   if (forced >= 0) return forced;
   const long long avg_rows = p.m / (p.num_local > 0 ? p.num_local : 1);
   if (avg_rows <= 48) return kT64x128;
@@ -1530,7 +1728,7 @@ int pick_forward_tile(const GemmProblem& p, bool trans_rhs) {
 // co-resident 128 x 256 workgroups per CU with 3-slot rings of 32-deep stages
 // (one workgroup multiplies while the other drains its dW stores).
 int pick_trans_tile(const GemmProblem& p) {
-  const int forced = forced_tile("RD_TRANS_TILE");
+  const int forced = forced_tile(RD_TUNE_TRANS_TILE);
   if (forced >= 0) return forced;
   return p.k >= 128 && p.n >= 256 ? kT128x256s3x2 : kT128x128x2;
 }
@@ -1542,6 +1740,11 @@ void launch_one(const KArgs& a, long long work, hipStream_t stream) {
     grouped_gemm_regs<MODE, BM, BN><<<grid_size(work, 2), kThreads, 0, stream>>>(a);
   else
     grouped_gemm_stream<MODE, BM, BN, S, KS, WGS, MAXL, WR, WC><<<grid_size(work, WGS), WR * WC * 64, 0, stream>>>(a);
+}
+
+template <int MODE, int S, int KS>
+void launch_pp(const KArgs& a, long long work, hipStream_t stream) {
+  grouped_gemm_pp<MODE, S, KS><<<grid_size(work, 1), 512, 0, stream>>>(a);
 }
 
 template <int MODE>
@@ -1580,6 +1783,8 @@ void launch_tile(int tile, const KArgs& a, const GemmProblem& p, hipStream_t str
     case kW256x256k64: launch_one<MODE, 256, 256, 2, 64, 1, RD_MAX_GROUPS, 4, 2>(a, work(256, 256), stream); break;
     case kW128x512: launch_one<MODE, 128, 512, 3, 32, 1, RD_MAX_GROUPS, 2, 4>(a, work(128, 512), stream); break;
     case kW128x256k32: launch_one<MODE, 128, 256, 6, 32, 1, RD_MAX_GROUPS, 2, 4>(a, work(128, 256), stream); break;
+    // eight waves in two ping-pong groups on 256 x 256 tiles, a 2-slot ring of 64-deep stages
+    case kP256x256: launch_pp<MODE, 2, 64>(a, work(256, 256), stream); break;
     default: launch_one<MODE, 128, 128, 4, 64>(a, work(128, 128), stream); break;
   }
 }
@@ -1593,11 +1798,10 @@ bool fits_32bit(long long a, long long b) { return a * b * 2 < (1ll << 32); }
 // 256-column strips and k into 16-row steps.  One workgroup per CU; the
 // workspace holds seg_max partial blocks per workgroup, seg_max bounding the
 // blocks one range can touch (from at most ceil(m/32) + num_local row blocks);
-// it must fit in 256 MiB.  RD_DECODE=0 turns the path off (for sweeps).
+// it must fit in 256 MiB.  rd_tune_set(RD_TUNE_DECODE, 0) turns the path off (for sweeps).
 DecodePlan plan_decode_impl(const GemmProblem& p, bool trans_rhs) {
   DecodePlan d{};
-  const char* env = getenv("RD_DECODE");
-  if (trans_rhs || (env != nullptr && env[0] == '0')) return d;
+  if (trans_rhs || g_tune[RD_TUNE_DECODE].load(std::memory_order_relaxed) == 0) return d;
   const long long avg_rows = p.m / (p.num_local > 0 ? p.num_local : 1);
   if (p.m <= 0 || avg_rows > 24 || p.k % kDecKS != 0 || !fits_32bit(p.m, p.k) || !fits_32bit(p.k, p.n)) return d;
   const int nb = p.n % 768 == 0 ? 6 : p.n % 512 == 0 ? 4 : p.n % 256 == 0 ? 2 : 0;
@@ -1675,7 +1879,7 @@ int launch_forward_glu(const GemmProblem& p, hipStream_t stream) {
     return (static_cast<long long>((p.m + BM - 1) / BM) + p.num_local) * ((p.n + TN - 1) / TN) +
            (p.m + kZeroRows - 1) / kZeroRows + 2;
   };
-  int tile = forced_tile("RD_FWD_TILE");
+  int tile = forced_tile(RD_TUNE_FWD_TILE);
   if (tile == kW128x512 && p.n % 256 != 0) tile = -1;  // the 512-column tile needs h % 256 == 0
   if (tile != kT64x128 && tile != kT128x256 && tile != kT128x256x2 && tile != kW128x256 && tile != kW128x512) {
     const long long avg_rows = p.m / (p.num_local > 0 ? p.num_local : 1);
@@ -1750,15 +1954,30 @@ int launch_trans(const GemmProblem& p, hipStream_t stream) {
 }
 
 int device_cu_count() {
-  static int cache[64] = {0};
+  // one entry per device, filled on first use; concurrent first calls store the same value
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cache[dev] == 0) {
-    int v = 0;
+  int v = cache[dev].load(std::memory_order_acquire);
+  if (v == 0) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    cache[dev] = v;
+    cache[dev].store(v, std::memory_order_release);
   }
-  return cache[dev];
+  return v;
 }
+
+int tune_set(int which, int value) {
+  if (which == RD_TUNE_FWD_TILE || which == RD_TUNE_TRANS_TILE) {
+    if (value < -1 || value >= kTileCount) return RD_EINVAL;
+  } else if (which == RD_TUNE_DECODE) {
+    if (value != 0 && value != 1) return RD_EINVAL;
+  } else {
+    return RD_EINVAL;
+  }
+  g_tune[which].store(value, std::memory_order_relaxed);
+  return RD_OK;
+}
+
+int tile_count() { return kTileCount; }
 
 }  // namespace rd

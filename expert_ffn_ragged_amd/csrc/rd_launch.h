@@ -52,7 +52,14 @@ int launch_glu_bwd(const void* fused, const void* d_out, const int32_t* limit, v
 int launch_unsort_bwd_rows(const void* g, const void* y, const float* w, const int32_t* limit, void* grad,
                            float* dot, int rows, int hidden, hipStream_t stream);
 
-// Number of compute units of the current device (cached per device).
+// Rows [clamp(*limit, 0, rows), rows) of a [rows, row_bytes] buffer set to zero (row_bytes % 16 == 0).
+int launch_zero_rows(void* buf, const int32_t* limit, long long rows, long long row_bytes, hipStream_t stream);
+
+// Number of compute units of the current device (cached per device, thread-safe).
 int device_cu_count();
+
+// Tuning overrides (rd_tune_set) and the number of grouped-GEMM tile shapes.
+int tune_set(int which, int value);
+int tile_count();
 
 }  // namespace rd

@@ -10,10 +10,14 @@
 //
 // One wave64 owns a row: lane l handles the 16-byte chunks l, l + 64, ... of
 // it (128-bit non-temporal loads of g and y and stores of the gradient, eight
-// chunks in flight per lane), keeps its part of the dot in float32, and the
-// wave adds the 64 parts in a fixed butterfly order.  A row's dot is therefore
-// produced by exactly one wave: no partial sums cross workgroups, no atomics,
-// and the result is the same on every run.  A persistent grid of waves (32
+// chunks in flight per lane), keeps its part of the dot in float64, and the
+// wave adds the 64 parts in a fixed butterfly order before one rounding to
+// float32.  Each product of two bf16 values is exact in float32, and a
+// float64 sum of a few thousand of them is within about 1e-12 relative of the
+// exact dot, so the float32 result is the exact dot rounded once (within half
+// a float32 ulp), whatever the order.  A row's dot is produced by exactly one
+// wave: no partial sums cross workgroups, no atomics, and the result is the
+// same on every run.  A persistent grid of waves (32
 // workgroups per CU) strides over the valid rows.  HBM-bound: 3 * 2 * hidden + 8 bytes per row.
 #include "rd_device.h"
 #include "rd_launch.h"
@@ -45,9 +49,10 @@ __device__ __forceinline__ uint32_t grad_word(uint32_t gw, float w) {
   return pack_bf16x2(a, b);
 }
 
-__device__ __forceinline__ float dot_word(uint32_t gw, uint32_t yw, float acc) {
-  acc += bf_lo(gw) * bf_lo(yw);
-  acc += bf_hi(gw) * bf_hi(yw);
+// Exact float32 products (8-bit significands), accumulated in float64.
+__device__ __forceinline__ double dot_word(uint32_t gw, uint32_t yw, double acc) {
+  acc += static_cast<double>(bf_lo(gw) * bf_lo(yw));
+  acc += static_cast<double>(bf_hi(gw) * bf_hi(yw));
   return acc;
 }
 
@@ -70,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void unsort_bwd_rows_kernel(const uint16_
     const uint4* gr = reinterpret_cast<const uint4*>(g + static_cast<long long>(r) * hidden);
     const uint4* yr = reinterpret_cast<const uint4*>(y + static_cast<long long>(r) * hidden);
     uint4* dr = reinterpret_cast<uint4*>(grad + static_cast<long long>(r) * hidden);
-    float acc = 0.0f;
+    double acc = 0.0;
     int c = lane;
     for (; c + 64 * (kUnroll - 1) < chunks; c += 64 * kUnroll) {
       uint4 gv[kUnroll], yv[kUnroll];
@@ -100,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void unsort_bwd_rows_kernel(const uint16_
     }
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d, 64);
-    if (lane == 0) dot[r] = acc;
+    if (lane == 0) dot[r] = static_cast<float>(acc);
   }
 }
 

@@ -36,9 +36,12 @@ XCDS = 8
 
 # bench.py op name <- kernel name pattern (one kernel per op in the step)
 OP_OF_KERNEL = (
-    (r"grouped_gemm_stream<0,", "ragged_dot"),
-    (r"grouped_gemm_stream<1,", "ragged_dot_trans_rhs"),
-    (r"grouped_gemm_stream<2,", "trans_ragged_dot"),
+    (r"grouped_gemm_(stream|pp|regs)<0,", "ragged_dot"),
+    (r"grouped_gemm_(stream|pp|regs)<1,", "ragged_dot_trans_rhs"),
+    (r"grouped_gemm_(stream|pp|regs)<2,", "trans_ragged_dot"),
+    (r"grouped_gemm_(stream|pp)<4,", "ragged_dot_glu"),
+    (r"unsort_bwd_rows_kernel", "unsort_bwd_rows"),
+    (r"zero_rows_kernel", "zero_rows_from_limit"),
     (r"glu_fwd_kernel", "glu_fwd"),
     (r"glu_bwd_kernel", "glu_bwd"),
     (r"decode_streamk_gemm", "decode_gemm"),
@@ -98,13 +101,16 @@ def counter_means(directory):
     return means, cal
 
 
-def traffic_summary(fetch_dir, write_dir, mfma_dir, command):
+DEFAULT_TITLE = "MoE up-projection fwd+bwd step (m8192 k4096 n2048 g64 Zipf 1.1), MI355X"
+
+
+def traffic_summary(fetch_dir, write_dir, mfma_dir, command, title=DEFAULT_TITLE):
     fm, fcal = counter_means(fetch_dir)
     wm, wcal = counter_means(write_dir)
     fscale = CALIB_BYTES / (fcal["FETCH_SIZE"] * 1024)
     wscale = CALIB_BYTES / (wcal["WRITE_SIZE"] * 1024)
     lines = [
-        "# HBM traffic per launch: MoE up-projection fwd+bwd step (m8192 k4096 n2048 g64 Zipf 1.1), MI355X",
+        f"# HBM traffic per launch: {title}",
         "",
         "Commands (run from the repository root on the GPU box with `TMPDIR=/tmp` exported; one counter",
         "per run, each run its own process):",
@@ -223,7 +229,7 @@ PER_CU = ("TCP_PENDING_STALL_CYCLES", "TCP_UTCL1_STALL_INFLIGHT_MAX", "TA_TA_BUS
 CUS = 256
 
 
-def loadpath_summary(dirs, command):
+def loadpath_summary(dirs, command, title=DEFAULT_TITLE):
     """Load-path counters of the step's kernels: per-CU busy / stall fractions (counter summed over the
     256 CUs / (GRBM_GUI_ACTIVE / 8 XCDs x 256)), the mean L1 -> L2 read latency
     (TCP_TCC_READ_REQ_LATENCY / (TCC_HIT + TCC_MISS)) and the L2 hit rate."""
@@ -232,7 +238,7 @@ def loadpath_summary(dirs, command):
         m, _ = counter_means(d)
         for (name, ctr), (val, _n) in m.items():
             means.setdefault(name, {}).setdefault(ctr, []).append(val)
-    lines = ["# Load-path counters: MoE up-projection fwd+bwd step (m8192 k4096 n2048 g64 Zipf 1.1), MI355X", "",
+    lines = [f"# Load-path counters: {title}", "",
              "Commands (run from the repository root on the GPU box with `TMPDIR=/tmp` exported; one counter set "
              "per run):", "", "```", command, "```", "",
              f"source digest: {source_digest()}", "",
@@ -282,6 +288,7 @@ def main():
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
     t.add_argument("--mfma")
+    t.add_argument("--title", default=DEFAULT_TITLE)
     t.add_argument("--command", required=True)
     t.add_argument("--out", required=True)
     s = sub.add_parser("stats")
@@ -291,6 +298,7 @@ def main():
     s.add_argument("--out", required=True)
     lp = sub.add_parser("loadpath")
     lp.add_argument("--dirs", nargs="+", required=True)
+    lp.add_argument("--title", default=DEFAULT_TITLE)
     lp.add_argument("--command", required=True)
     lp.add_argument("--out", required=True)
     r = sub.add_parser("apitrace")
@@ -299,9 +307,9 @@ def main():
     r.add_argument("--out", required=True)
     a = ap.parse_args()
     if a.what == "traffic":
-        text = traffic_summary(a.fetch, a.write, a.mfma, a.command)
+        text = traffic_summary(a.fetch, a.write, a.mfma, a.command, a.title)
     elif a.what == "loadpath":
-        text = loadpath_summary(a.dirs, a.command)
+        text = loadpath_summary(a.dirs, a.command, a.title)
     elif a.what == "apitrace":
         text = apitrace_summary(a.trace, a.command)
     else:

@@ -10,6 +10,7 @@ shape ``(1,)`` on the GPU, and ``group_sizes`` as an int32 GPU tensor, so a
 call never reads device data on the host and can be captured in a HIP graph.
 """
 
+import contextlib
 import ctypes
 import os
 
@@ -18,7 +19,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librd.so")
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 RD_OK, RD_EINVAL, RD_EUNSUPPORTED, RD_EHIP = 0, 1, 2, 3
 RD_BF16, RD_F32 = 0, 1
 _DTYPES = {torch.bfloat16: RD_BF16, torch.float32: RD_F32}
@@ -38,7 +39,11 @@ EXPORTS = (
     "rd_glu_fwd",
     "rd_glu_bwd",
     "rd_unsort_bwd_rows",
+    "rd_zero_rows_from_limit",
+    "rd_tune_set",
+    "rd_tune_tile_count",
 )
+RD_TUNE_FWD_TILE, RD_TUNE_TRANS_TILE, RD_TUNE_DECODE = 0, 1, 2
 
 
 class RDError(RuntimeError):
@@ -82,6 +87,12 @@ def library():
     lib.rd_glu_bwd.argtypes = [vp, vp, vp, vp, i64, i64, vp]
     lib.rd_unsort_bwd_rows.restype = ctypes.c_int
     lib.rd_unsort_bwd_rows.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, vp]
+    lib.rd_zero_rows_from_limit.restype = ctypes.c_int
+    lib.rd_zero_rows_from_limit.argtypes = [vp, vp, i64, i64, vp]
+    lib.rd_tune_set.restype = ctypes.c_int
+    lib.rd_tune_set.argtypes = [i32, i32]
+    lib.rd_tune_tile_count.restype = ctypes.c_int
+    lib.rd_tune_tile_count.argtypes = []
     if lib.rd_abi_version() != ABI_VERSION:
         raise RDError("librd.so ABI version mismatch")
     _lib = lib
@@ -101,6 +112,40 @@ def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _on_stream(stream, *tensors):
+    """Tie tensors allocated here (torch's current stream) to the stream the kernels run on, so the
+    caching allocator does not hand their memory out again before that stream is done with them."""
+    if stream is None:
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
+def tile_count():
+    """Number of grouped-GEMM tile shapes ``tuning`` accepts."""
+    return library().rd_tune_tile_count()
+
+
+@contextlib.contextmanager
+def tuning(fwd_tile=None, trans_tile=None, decode=None):
+    """Force tile shapes (0 .. tile_count() - 1) or turn the decode split path off (decode=False) for
+    the calls made inside the block, for tile sweeps; the built-in choices come back on exit.
+    Process-wide (rd_tune_set), so not for concurrent use from several threads."""
+    lib = library()
+    sets = [(RD_TUNE_FWD_TILE, fwd_tile), (RD_TUNE_TRANS_TILE, trans_tile),
+            (RD_TUNE_DECODE, None if decode is None else int(bool(decode)))]
+    try:
+        for key, val in sets:
+            if val is not None:
+                _check(lib.rd_tune_set(key, int(val)))
+        yield
+    finally:
+        lib.rd_tune_set(RD_TUNE_FWD_TILE, -1)
+        lib.rd_tune_set(RD_TUNE_TRANS_TILE, -1)
+        lib.rd_tune_set(RD_TUNE_DECODE, 1)
 
 
 def _need(t, name, dtype, ndim=None):
@@ -150,6 +195,7 @@ def ragged_dot(x, w, group_sizes, group_offset=None, limit=None, trans_rhs=False
         kw, n = w.shape[1], w.shape[2]
     if kw != k:
         raise ValueError("contraction sizes of x and w differ")
+    fresh = out is None
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=x.device)
     _need(out, "out", out.dtype, 2)
@@ -159,6 +205,9 @@ def ragged_dot(x, w, group_sizes, group_offset=None, limit=None, trans_rhs=False
     ws_bytes = lib.rd_forward_workspace_size(m, k, n, gl, 1 if trans_rhs else 0)
     if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+        _on_stream(stream, workspace)
+    if fresh:
+        _on_stream(stream, out)
     fn = lib.rd_forward_trans_rhs if trans_rhs else lib.rd_forward
     _check(fn(_ptr(x), _ptr(w), _ptr(group_sizes), group_sizes.numel(), _ptr(group_offset), gl,
               _ptr(limit), _ptr(out), _DTYPES[out.dtype], m, k, n,
@@ -187,6 +236,7 @@ def ragged_dot_fp8(x, w, group_sizes, group_offset=None, limit=None, trans_rhs=F
         raise ValueError("contraction sizes of x and w differ")
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=x.device)
+        _on_stream(stream, out)
     _need(out, "out", out.dtype, 2)
     if tuple(out.shape) != (m, n) or out.dtype not in _DTYPES:
         raise ValueError("out must be [m, n] bf16 or float32")
@@ -214,6 +264,7 @@ def trans_ragged_dot_fp8(x, dy, group_sizes, num_local=None, group_offset=None, 
     gl = group_sizes.numel() if num_local is None else int(num_local)
     if out is None:
         out = torch.empty((gl, k, n), dtype=out_dtype, device=x.device)
+        _on_stream(stream, out)
     _need(out, "out", out.dtype, 3)
     if tuple(out.shape) != (gl, k, n) or out.dtype not in _DTYPES:
         raise ValueError("out must be [num_local, k, n] bf16 or float32")
@@ -247,11 +298,13 @@ def ragged_dot_glu(x, wi, group_sizes, group_offset=None, limit=None, act=None, 
     h = h2 // 2
     if act is None:
         act = torch.empty((m, h), dtype=torch.bfloat16, device=x.device)
+        _on_stream(stream, act)
     _need(act, "act", torch.bfloat16, 2)
     if tuple(act.shape) != (m, h):
         raise ValueError("act must be [m, h]")
     if fused is None and want_fused:
         fused = torch.empty((m, h2), dtype=torch.bfloat16, device=x.device)
+        _on_stream(stream, fused)
     if fused is not None:
         _need(fused, "fused", torch.bfloat16, 2)
         if tuple(fused.shape) != (m, h2):
@@ -274,6 +327,7 @@ def trans_ragged_dot(x, dy, group_sizes, num_local=None, group_offset=None, limi
         raise ValueError("x and dy must have the same rows")
     n = dy.shape[1]
     gl = group_sizes.numel() if num_local is None else int(num_local)
+    fresh = out is None
     if out is None:
         out = torch.empty((gl, k, n), dtype=out_dtype, device=x.device)
     _need(out, "out", out.dtype, 3)
@@ -283,6 +337,9 @@ def trans_ragged_dot(x, dy, group_sizes, num_local=None, group_offset=None, limi
     ws_bytes = lib.rd_trans_workspace_size(m, k, n, gl)
     if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+        _on_stream(stream, workspace)
+    if fresh:
+        _on_stream(stream, out)
     _check(lib.rd_trans(_ptr(x), _ptr(dy), _ptr(group_sizes), group_sizes.numel(), _ptr(group_offset), gl,
                         _ptr(limit), _ptr(out), _DTYPES[out.dtype], m, k, n,
                         _ptr(workspace) if ws_bytes else None, ws_bytes, _stream(stream)))
@@ -299,6 +356,7 @@ def glu_fwd(fused, limit=None, out=None, stream=None):
     h = two_h // 2
     if out is None:
         out = torch.empty((rows, h), dtype=torch.bfloat16, device=fused.device)
+        _on_stream(stream, out)
     _need(out, "out", torch.bfloat16, 2)
     if tuple(out.shape) != (rows, h):
         raise ValueError("out must be [rows, h]")
@@ -317,6 +375,7 @@ def glu_bwd(fused, d_out, limit=None, out=None, stream=None):
         raise ValueError("d_out must be [rows, h]")
     if out is None:
         out = torch.empty((rows, two_h), dtype=torch.bfloat16, device=fused.device)
+        _on_stream(stream, out)
     _need(out, "out", torch.bfloat16, 2)
     if tuple(out.shape) != (rows, two_h):
         raise ValueError("out must be [rows, 2h]")
@@ -339,8 +398,10 @@ def unsort_bwd_rows(g, y, w, limit=None, grad=None, dot=None, stream=None):
         raise ValueError("g and y must be [rows, hidden] and w [rows]")
     if grad is None:
         grad = torch.empty((rows, hidden), dtype=torch.bfloat16, device=g.device)
+        _on_stream(stream, grad)
     if dot is None:
         dot = torch.empty((rows,), dtype=torch.float32, device=g.device)
+        _on_stream(stream, dot)
     _need(grad, "grad", torch.bfloat16, 2)
     _need(dot, "dot", torch.float32, 1)
     if tuple(grad.shape) != (rows, hidden) or dot.shape[0] != rows:
@@ -348,3 +409,18 @@ def unsort_bwd_rows(g, y, w, limit=None, grad=None, dot=None, stream=None):
     _check(library().rd_unsort_bwd_rows(_ptr(g), _ptr(y), _ptr(w), _ptr(limit), _ptr(grad), _ptr(dot), rows, hidden,
                                         _stream(stream)))
     return grad, dot
+
+
+def zero_rows_from_limit(buf, limit, stream=None):
+    """Rows at or past ``limit`` (a (1,) int32 GPU tensor; None: nothing to do) of ``buf`` set to +0,
+    in place; ``buf`` is a contiguous GPU tensor whose first dim is the rows.  Returns ``buf``."""
+    if limit is None:
+        return buf
+    limit = _scalar(limit, "limit")
+    if buf.device.type != "cuda" or not buf.is_contiguous() or buf.dim() < 1:
+        raise ValueError("buf must be a contiguous GPU tensor")
+    rows = buf.shape[0]
+    row_bytes = buf[0].numel() * buf.element_size() if rows else 16
+    _check(library().rd_zero_rows_from_limit(_ptr(buf) if rows else None, _ptr(limit), rows, row_bytes,
+                                             _stream(stream)))
+    return buf

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define RD_ABI_VERSION 5
+#define RD_ABI_VERSION 6
 
 /* status codes */
 #define RD_OK 0
@@ -272,8 +272,10 @@ int rd_glu_bwd(const void* fused, const void* d_out, const int32_t* limit, void*
  *   grad  [rows, hidden] bf16: grad[r, c] = bf16(f32(g[r, c]) * w[r]), a
  *         float32 product rounded once to bf16 (RNE).
  *   dot   [rows] float32: dot[r] = sum_c f32(g[r, c]) * f32(y[r, c]), the
- *         routing-weight gradient, summed in float32 in a fixed order (the
- *         same on every run; the page leaves the order free).
+ *         routing-weight gradient: exact products summed in float64 in a
+ *         fixed order and rounded once to float32 (within half a float32
+ *         ulp of the exact dot; the same on every run; the page leaves the
+ *         summation free and checks it with an absolute tolerance of 1e-4).
  *
  * Rows r >= L = clamp(*limit, 0, rows) are neither read nor written (in any
  * of the five arrays).  hidden > 0 and a multiple of 8; g, y, grad 16-byte
@@ -282,6 +284,46 @@ int rd_glu_bwd(const void* fused, const void* d_out, const int32_t* limit, void*
  */
 int rd_unsort_bwd_rows(const void* g, const void* y, const float* w, const int32_t* limit, void* grad, float* dot,
                        int64_t rows, int64_t hidden, void* stream);
+
+/*
+ * Rows at or past the valid-row limit set to +0 ([MaxText]: the packed
+ * expert buffer's kernels touch only rows [0, limit), limit a device
+ * scalar).  Rows r >= L = clamp(*limit, 0, rows) of the [rows, row_bytes]
+ * buffer buf get all-zero bytes; rows below L are not touched.  Used for the
+ * gradients of a packed buffer's inputs, which are exactly zero past the
+ * limit (those rows take no part in the computation).  limit NULL means
+ * L = rows: nothing is written or launched.  row_bytes > 0 and a multiple of
+ * 16 (else RD_EUNSUPPORTED); buf 16-byte aligned; with rows == 0 nothing is
+ * launched and buf may be NULL.
+ */
+int rd_zero_rows_from_limit(void* buf, const int32_t* limit, int64_t rows, int64_t row_bytes, void* stream);
+
+/*
+ * Tuning hook, for tile sweeps (the pages ask whether benchmarking and
+ * tuning code should ship with the kernels: SkyRL-tx PR #867, "Todo /
+ * Questions"); not needed for correct results.  Sets a process-wide override
+ * read by later calls:
+ *   RD_TUNE_FWD_TILE   the grouped-GEMM tile shape of rd_forward,
+ *                      rd_forward_trans_rhs and rd_forward_glu (value in
+ *                      [0, rd_tune_tile_count()), or -1 for the built-in
+ *                      choice from m, k, n and num_local);
+ *   RD_TUNE_TRANS_TILE the same for rd_trans;
+ *   RD_TUNE_DECODE     1 (default) allows the split-contraction decode path
+ *                      of rd_forward, 0 turns it off.
+ * Every shape computes the same results within the GEMM tolerance (the
+ * contraction order within a tile is the same, so outputs agree bitwise in
+ * practice).  rd_forward_glu ignores forced shapes it has no fused form of.
+ * Returns RD_OK, or RD_EINVAL for an unknown key or an out-of-range value.
+ * Thread-safe; a call in flight on another thread sees the old or the new
+ * value.
+ */
+#define RD_TUNE_FWD_TILE 0
+#define RD_TUNE_TRANS_TILE 1
+#define RD_TUNE_DECODE 2
+int rd_tune_set(int32_t which, int32_t value);
+
+/* Number of grouped-GEMM tile shapes RD_TUNE_FWD_TILE / RD_TUNE_TRANS_TILE accept. */
+int rd_tune_tile_count(void);
 
 #ifdef __cplusplus
 }

@@ -3,8 +3,8 @@
 bfloat16 is the upper half of an IEEE-754 binary32: widening is a 16-bit
 shift and is exact; narrowing rounds to nearest, ties to even (RNE), with NaN
 kept NaN (quieted).  Both pages that fix output precision round once, at the
-end, to bf16 (MaxText PR #5760, commit "valid-rows-only MoE kernels": the GLU
-"rounding only the outputs").
+end, to bf16 (MaxText PR #5760, commit on valid rows: the GLU keeps float32
+throughout and narrows its result a single time).
 """
 
 import numpy as np

@@ -20,9 +20,9 @@ backward):
 Readings (listed in the design doc): rows at or past ``L = clamp(limit, 0,
 rows)`` are neither read nor written (the page's kernel also writes zeros up
 to the end of the 1024-row block holding row ``limit - 1``; that is an
-artifact of its block size, not part of what it computes, and the plainest
-contract consistent with the page's "rows left unwritten are never read" is
-to leave them untouched, as the other kernels here do).  The dot is returned
+artifact of its block size, not part of what it computes; since the page
+states that nothing downstream consumes the rows it leaves unwritten, the
+plainest contract is to leave them untouched, as the other kernels here do).  The dot is returned
 as the float64 sum of the exact products (every product of two bf16 values
 is exact in float64), the value any float32 summation order approximates.
 """

@@ -46,7 +46,7 @@ def test_links_the_same_hip_runtime_soname_as_torch():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.rd_abi_version() == rd.ABI_VERSION == 5
+    assert lib.rd_abi_version() == rd.ABI_VERSION == 6
     for s in (0, 1, 2, 3, 99):
         assert isinstance(lib.rd_status_string(s), bytes)
     assert lib.rd_trans_workspace_size(100, 64, 64, 4) == 0
@@ -165,3 +165,19 @@ def test_fp8_forms_reject_bad_sizes(lib):
         assert call(fn, k=0) == rd.RD_EINVAL
         assert call(fn, m=0) == rd.RD_OK
     assert call(lib.rd_forward_fp8, n=24) == rd.RD_EUNSUPPORTED
+
+
+def test_tuning_hook_validates_and_restores(lib):
+    n = lib.rd_tune_tile_count()
+    assert n >= 19
+    assert lib.rd_tune_set(rd.RD_TUNE_FWD_TILE, n) == rd.RD_EINVAL
+    assert lib.rd_tune_set(rd.RD_TUNE_TRANS_TILE, -2) == rd.RD_EINVAL
+    assert lib.rd_tune_set(rd.RD_TUNE_DECODE, 2) == rd.RD_EINVAL
+    assert lib.rd_tune_set(7, 0) == rd.RD_EINVAL
+    with rd.tuning(fwd_tile=n - 1, trans_tile=0, decode=False):
+        pass
+    with pytest.raises(rd.RDError):
+        with rd.tuning(fwd_tile=n):
+            pass
+    # the built-in choices are back (no effect is observable without a GPU; the calls succeed)
+    assert lib.rd_tune_set(rd.RD_TUNE_FWD_TILE, -1) == rd.RD_OK

@@ -156,3 +156,73 @@ def test_trans_ragged_dot_backward_rules():
     assert_gemm_close(dy32.cpu().numpy(), oracle.ragged_dot(xb, dzb, gs_host), "dy")
     assert_bf16_is_rne_of_f32(dx, dx32, "dx")
     assert_bf16_is_rne_of_f32(dy, dy32, "dy")
+
+
+@pytest.mark.parametrize("which", ["ragged_dot", "ragged_dot_trans_rhs", "trans_ragged_dot", "moe_mlp"])
+def test_input_gradients_are_zero_past_the_limit(which):
+    """Rows at or past the limit take no part in the computation: their input gradient is exactly +0,
+    whatever the gradient buffer's memory held before (it is recycled from a NaN-filled block)."""
+    say(f"gradient tail past the limit: {which}")
+    G, k, n = 4, 128, 192
+    gs_host = workloads.random_sizes(G, 400, seed=91, empty=(2,))
+    m = int(gs_host.sum()) + 30
+    L = int(gs_host.sum()) - 57
+    gs = torch.from_numpy(gs_host).to(DEV)
+    limt = dev_i32(L)
+    # leave NaN bit patterns in the allocator's free blocks of the sizes the gradients take
+    junk = [torch.full((m, c), float("nan"), dtype=torch.bfloat16, device=DEV) for c in (k, n, 2 * n)]
+    del junk
+    x = bf16_normal((m, k), 1.0, 92, DEV).requires_grad_(True)
+    if which == "moe_mlp":
+        wi = bf16_normal((G, k, 2 * n), 0.05, 93, DEV).requires_grad_(True)
+        wo = bf16_normal((G, n, k), 0.05, 94, DEV).requires_grad_(True)
+        out = ag.moe_mlp(x, wi, wo, gs, None, limt)
+        grads = torch.autograd.grad(out, (x,), bf16_normal(out.shape, 1.0, 95, DEV))
+    elif which == "trans_ragged_dot":
+        y = bf16_normal((m, n), 1.0, 93, DEV).requires_grad_(True)
+        z = ag.trans_ragged_dot(x, y, gs, None, None, limt)
+        grads = torch.autograd.grad(z, (x, y), bf16_normal(z.shape, 0.1, 95, DEV))
+    else:
+        trans_rhs = which.endswith("trans_rhs")
+        w = bf16_normal((G, n, k) if trans_rhs else (G, k, n), 0.1, 93, DEV).requires_grad_(True)
+        out = ag.ragged_dot(x, w, gs, None, limt, trans_rhs=trans_rhs)
+        grads = torch.autograd.grad(out, (x,), bf16_normal(out.shape, 1.0, 95, DEV))
+    torch.cuda.synchronize()
+    for gr in grads:
+        assert gr.shape[0] == m
+        assert bool((gr[L:].view(torch.int16) == 0).all()), f"{which}: rows past the limit are not +0"
+        assert bool(torch.isfinite(gr[:L].float()).all()), f"{which}: non-finite gradient below the limit"
+
+
+@pytest.mark.parametrize("limit", [None, -5, 0, 17, 300, 1000])
+def test_zero_rows_from_limit(limit):
+    say(f"zero_rows_from_limit limit={limit}")
+    rows = 300
+    for dtype, cols in ((torch.bfloat16, 72), (torch.float32, 36), (torch.bfloat16, 4096)):
+        buf = bf16_normal((rows, cols), 1.0, 96, DEV).to(dtype)
+        before = buf.clone()
+        rd.zero_rows_from_limit(buf, None if limit is None else dev_i32(limit))
+        torch.cuda.synchronize()
+        L = rows if limit is None else min(max(limit, 0), rows)
+        assert torch.equal(buf[:L], before[:L])
+        assert bool((buf[L:].view(torch.int16 if dtype == torch.bfloat16 else torch.int32) == 0).all())
+
+
+def test_calls_on_a_side_stream():
+    """A call given stream= runs there; outputs and the decode workspace it allocates stay reserved for
+    that stream (the caching allocator does not reuse them while the side stream still works)."""
+    say("decode ragged_dot on a side stream")
+    d = workloads.make(5, DEV, parts=("x", "w"))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    ref = rd.ragged_dot(d["x"], d["w"], d["gs"])
+    torch.cuda.synchronize()
+    outs = []
+    for _ in range(3):
+        outs.append(rd.ragged_dot(d["x"], d["w"], d["gs"], stream=side))
+        # allocations on the current stream in between must not land on the side stream's buffers
+        tmp = torch.full((d["m"], d["n"]), 7.0, dtype=torch.bfloat16, device=DEV)
+        del tmp
+    side.synchronize()
+    for o in outs:
+        assert torch.equal(o.view(torch.int16), ref.view(torch.int16))

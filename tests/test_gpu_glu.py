@@ -8,12 +8,15 @@ import oracle
 from expert_ffn_ragged_amd import rd, workloads
 from expert_ffn_ragged_amd.workloads import bf16_normal, bits
 from oracle.bf16 import f32_to_bf16_bits
-from tests.gpu_util import assert_glu_close, is_sentinel, say, sentinel
+from tests.gpu_util import assert_glu_close, bf16_nan, is_sentinel, say, sentinel
 from tests.test_oracle_glu import FWD_TABLE
 
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
+# largest fraction of GLU outputs allowed to differ (by the one ulp the tolerance permits) from the
+# oracle's correctly rounded float32 evaluation over the all-gate sweep
+GLU_NOT_BIT_EQUAL_MAX = 1e-5  # measured on MI355X: 4.1e-6 (forward), 3.5e-6 (backward)
 
 
 def to_dev(bits16):
@@ -39,9 +42,18 @@ def test_every_gate_pattern():
     torch.cuda.synchronize()
     got_f = bits(out)
     got_b = bits(dg)
-    assert_glu_close(got_f, oracle.glu_fwd(fused), "glu fwd sweep")
-    assert_glu_close(got_b, oracle.glu_bwd(fused, d_out), "glu bwd sweep")
+    want_f, want_b = oracle.glu_fwd(fused), oracle.glu_bwd(fused, d_out)
+    assert_glu_close(got_f, want_f, "glu fwd sweep")
+    assert_glu_close(got_b, want_b, "glu bwd sweep")
     assert not np.any(got_b == 0x8000)
+    # the 1-ulp rule is the tolerance; how often the hardware exp2 / reciprocal path is not bit-equal to
+    # the correctly rounded float32 evaluation is recorded and bounded here (the DESIGN notes give it)
+    both_nan_f = bf16_nan(got_f) & bf16_nan(want_f)
+    both_nan_b = bf16_nan(got_b) & bf16_nan(want_b)
+    frac_f = float(np.mean((got_f != want_f) & ~both_nan_f & ~((got_f | want_f) == 0x8000)))
+    frac_b = float(np.mean((got_b != want_b) & ~both_nan_b))
+    say(f"glu all-gate sweep: not bit-equal to the oracle: fwd {frac_f:.3e}, bwd {frac_b:.3e}")
+    assert frac_f <= GLU_NOT_BIT_EQUAL_MAX and frac_b <= GLU_NOT_BIT_EQUAL_MAX, (frac_f, frac_b)
     # forward keeps IEEE signs: the same rows give -0 where the oracle gives -0
     want = oracle.glu_fwd(fused)
     assert np.array_equal(got_f[want == 0x8000], want[want == 0x8000])

@@ -63,10 +63,8 @@ def check_case(x, wi, gs_host, off, limit, what):
 
 @pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("window,limit_cut", [(False, None), (True, None), (True, 37), (False, 300)])
-def test_fused_equals_separate_kernels(monkeypatch, tile, window, limit_cut):
+def test_fused_equals_separate_kernels(tile, window, limit_cut):
     say(f"ragged_dot_glu tile={tile} window={window} limit_cut={limit_cut}")
-    if tile is not None:
-        monkeypatch.setenv("RD_FWD_TILE", tile)
     G, k, h = 6, 192, 256
     gs_host = workloads.random_sizes(G, 900, seed=61, empty=(2,))
     m = int(gs_host.sum()) + 40
@@ -74,37 +72,37 @@ def test_fused_equals_separate_kernels(monkeypatch, tile, window, limit_cut):
     x = bf16_normal((m, k), 1.0, 62, DEV)
     wi = bf16_normal((gl, k, 2 * h), 0.08, 63, DEV)
     limit = None if limit_cut is None else int(gs_host.sum()) - limit_cut
-    check_case(x, wi, gs_host, off, limit, f"tile {tile}")
+    with rd.tuning(fwd_tile=None if tile is None else int(tile)):
+        check_case(x, wi, gs_host, off, limit, f"tile {tile}")
 
 
 @pytest.mark.parametrize("tile", TILES)
-def test_fused_against_oracle_glu(monkeypatch, tile):
+def test_fused_against_oracle_glu(tile):
     """act is within 1 bf16 ulp of the oracle's GLU of the [gate | up] buffer, over the valid rows."""
     say(f"ragged_dot_glu oracle tile={tile}")
-    if tile is not None:
-        monkeypatch.setenv("RD_FWD_TILE", tile)
     G, k, h = 4, 128, 128
     gs_host = workloads.random_sizes(G, 500, seed=71, empty=(0,))
     m = int(gs_host.sum())
     x = bf16_normal((m, k), 2.0, 72, DEV)
     wi = bf16_normal((G, k, 2 * h), 0.5, 73, DEV)
     limit = m - 11
-    act, fused, L = check_case(x, wi, gs_host, None, limit, f"oracle tile {tile}")
+    with rd.tuning(fwd_tile=None if tile is None else int(tile)):
+        act, fused, L = check_case(x, wi, gs_host, None, limit, f"oracle tile {tile}")
     assert_glu_close(bits(act)[:L], oracle.glu_fwd(bits(fused), L), "act")
 
 
-def test_fused_decode_sized_groups(monkeypatch):
+def test_fused_decode_sized_groups():
     """Groups of a few rows (the 64-row tile), with empty groups and a window.  The reference runs
     ragged_dot on the tile kernels too: its split-contraction decode path (taken with a workspace)
     sums in another order, which the ragged_dot tests hold to the GEMM tolerance instead."""
     say("ragged_dot_glu decode-sized groups")
-    monkeypatch.setenv("RD_DECODE", "0")
     G, k, h = 32, 256, 384
     gs_host = workloads.random_sizes(G, 96, seed=81, empty=(0, 5, 6, 31))
     m = int(gs_host.sum())
     x = bf16_normal((m, k), 1.0, 82, DEV)
     wi = bf16_normal((24, k, 2 * h), 0.05, 83, DEV)
-    check_case(x, wi, gs_host, 4, None, "decode window")
+    with rd.tuning(decode=False):
+        check_case(x, wi, gs_host, 4, None, "decode window")
 
 
 def test_fused_no_rows_is_a_no_op():

@@ -1,7 +1,7 @@
 """Every grouped-GEMM tile shape against the oracle.
 
-The host picks a tile shape from m, k, n and num_local; RD_FWD_TILE and
-RD_TRANS_TILE force one (0..17, read at each call).  Each shape runs the
+The host picks a tile shape from m, k, n and num_local; the tuning hook
+(rd_tune_set, ``rd.tuning``) forces one.  Each shape runs the
 three GEMMs on one ragged case (groups against every tile edge, an empty
 group, a window and a limit with NaN rows past it) and must meet the same
 bar as the default choice: float32 output within the GEMM tolerance of the
@@ -21,7 +21,7 @@ from tests.gpu_util import assert_bf16_is_rne_of_f32, assert_gemm_close, is_pos_
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
-TILE_SHAPES = list(range(18))
+TILE_SHAPES = list(range(19))  # rd.tile_count() shapes; a test below checks the count
 
 GS = np.array([37, 0, 300, 129, 1, 200, 64], dtype=np.int32)
 M, K, N = int(GS.sum()) + 23, 320, 576
@@ -43,18 +43,17 @@ def case():
 
 
 @pytest.mark.parametrize("tile", TILE_SHAPES)
-def test_tile_shape_forward_forms(monkeypatch, case, tile):
+def test_tile_shape_forward_forms(case, tile):
     say(f"tile {tile} forward and trans_rhs")
-    monkeypatch.setenv("RD_FWD_TILE", str(tile))
-    monkeypatch.setenv("RD_DECODE", "0")
     x, w, wt, _ = case
     gs = torch.from_numpy(GS).to(DEV)
     lb, lo, hi, L = oracle.boundaries(GS, M, OFF, GL, LIMIT)
     for trans_rhs, wgt in ((False, w), (True, wt)):
         o32 = sentinel((M, N), torch.float32)
         o16 = sentinel((M, N), torch.bfloat16)
-        rd.ragged_dot(x, wgt, gs, dev_i32(OFF), dev_i32(LIMIT), trans_rhs=trans_rhs, out=o32)
-        rd.ragged_dot(x, wgt, gs, dev_i32(OFF), dev_i32(LIMIT), trans_rhs=trans_rhs, out=o16)
+        with rd.tuning(fwd_tile=tile, decode=False):
+            rd.ragged_dot(x, wgt, gs, dev_i32(OFF), dev_i32(LIMIT), trans_rhs=trans_rhs, out=o32)
+            rd.ragged_dot(x, wgt, gs, dev_i32(OFF), dev_i32(LIMIT), trans_rhs=trans_rhs, out=o16)
         torch.cuda.synchronize()
         what = f"tile {tile} trans_rhs={trans_rhs}"
         ref = oracle.ragged_dot(bits(x), bits(wgt), GS, OFF, LIMIT, trans_rhs)
@@ -65,18 +64,22 @@ def test_tile_shape_forward_forms(monkeypatch, case, tile):
 
 
 @pytest.mark.parametrize("tile", TILE_SHAPES)
-def test_tile_shape_trans_ragged_dot(monkeypatch, case, tile):
+def test_tile_shape_trans_ragged_dot(case, tile):
     say(f"tile {tile} trans_ragged_dot")
-    monkeypatch.setenv("RD_TRANS_TILE", str(tile))
     x, _, _, dy = case
     gs = torch.from_numpy(GS).to(DEV)
     d32 = sentinel((GL, K, N), torch.float32)
     d16 = sentinel((GL, K, N), torch.bfloat16)
-    rd.trans_ragged_dot(x, dy, gs, GL, dev_i32(OFF), dev_i32(LIMIT), out=d32)
-    rd.trans_ragged_dot(x, dy, gs, GL, dev_i32(OFF), dev_i32(LIMIT), out=d16)
+    with rd.tuning(trans_tile=tile):
+        rd.trans_ragged_dot(x, dy, gs, GL, dev_i32(OFF), dev_i32(LIMIT), out=d32)
+        rd.trans_ragged_dot(x, dy, gs, GL, dev_i32(OFF), dev_i32(LIMIT), out=d16)
     torch.cuda.synchronize()
     what = f"tile {tile} dW"
     ref = oracle.trans_ragged_dot(bits(x), bits(dy), GS, GL, OFF, LIMIT)
     assert_gemm_close(d32.cpu().numpy(), ref, what)
     assert_bf16_is_rne_of_f32(d16, d32, what)
     assert bool(is_pos_zero(d32[0]).all()) and bool(is_pos_zero(d16[0]).all()), what + ": empty group"
+
+
+def test_every_tile_shape_is_covered():
+    assert rd.tile_count() == len(TILE_SHAPES)

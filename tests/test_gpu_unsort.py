@@ -1,11 +1,13 @@
 """GPU parity of the weighted unsort backward (rd_unsort_bwd_rows) against the oracle.
 
-The gradient is compared bit for bit.  The routing-weight dot is float32
-summed in the kernel's fixed order (each lane adds its hidden/64 elements in
-sequence, then a 6-level butterfly over the 64 lanes), so its error is at
-most (hidden/64 + 6) float32 unit roundoffs times sum_c |g y| (each addition
-rounds once, with the product fused or exact); the test uses that bound.
-Rows at or past the limit must keep a sentinel pattern.
+The gradient is compared bit for bit.  The routing-weight dot adds exact
+products in float64 in the kernel's fixed order (each lane its hidden/64
+elements in sequence, then a 6-level butterfly over the 64 lanes) and rounds
+once to float32, so it is within half a float32 ulp of the exact dot plus
+(hidden/64 + 6) float64 unit roundoffs times sum_c |g y|; the test holds it
+to that bound and, as the MaxText page's own check of the same kernel does
+(PR #5760, the unsort_bwd_rows test), to an absolute 1e-4.  Rows at or past
+the limit must keep a sentinel pattern.
 """
 
 import numpy as np
@@ -20,7 +22,7 @@ from tests.gpu_util import is_sentinel, say, sentinel
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
-U32 = 2.0 ** -24
+U64 = 2.0 ** -53
 
 
 def dev_i32(v):
@@ -53,9 +55,12 @@ def check_rows(g, y, w, grad, dot, rows_idx, what):
     inf = np.isinf(ref_dot)
     assert np.array_equal(got_dot[inf], ref_dot[inf]), what + ": infinite dot mismatch"
     mag = (np.abs(oracle.bf16_bits_to_f64(gb[fin])) * np.abs(oracle.bf16_bits_to_f64(yb[fin]))).sum(axis=1)
-    bound = (hidden / 64 + 6) * U32 * mag + 1e-30
+    half_ulp = np.spacing(np.abs(ref_dot[fin]).astype(np.float32)).astype(np.float64) / 2
+    bound = half_ulp + (hidden / 64 + 6) * U64 * mag + 1e-45
     err = np.abs(got_dot[fin] - ref_dot[fin])
     assert np.all(err <= bound), f"{what}: dot error {err.max() if err.size else 0:.3e} over bound"
+    small = np.abs(ref_dot[fin]) < 1e3  # where an absolute tolerance means something for a float32 result
+    assert np.all(err[small] <= 1e-4), f"{what}: dot error {err[small].max():.3e} over the page's 1e-4"
 
 
 @pytest.mark.parametrize("hidden", [256, 4096])
