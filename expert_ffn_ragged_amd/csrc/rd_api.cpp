@@ -31,7 +31,7 @@ int check_dims(int64_t m, int64_t k, int64_t n) {
 int forward_common(const void* x, const void* w, const int32_t* group_sizes, int32_t num_groups,
                    const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* out,
                    int32_t out_dtype, int64_t m, int64_t k, int64_t n, void* workspace, size_t workspace_bytes,
-                   void* stream, bool trans_rhs) {
+                   void* stream, bool trans_rhs, bool noalloc = false) {
   int st = check_dims(m, k, n);
   if (st != RD_OK) return st;
   st = check_groups(num_groups, group_offset, num_local);
@@ -56,6 +56,7 @@ int forward_common(const void* x, const void* w, const int32_t* group_sizes, int
   p.m = static_cast<int>(m);
   p.k = static_cast<int>(k);
   p.n = static_cast<int>(n);
+  if (noalloc) return rd::launch_forward_noalloc(p, static_cast<hipStream_t>(stream));
   return rd::launch_forward(p, trans_rhs, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
@@ -82,6 +83,7 @@ const char* rd_status_string(int status) {
     case RD_EINVAL: return "invalid argument (null or misaligned pointer, bad size or dtype)";
     case RD_EUNSUPPORTED: return "unsupported size (k, n, h, hidden must be multiples of 8; dims < 2^31; groups <= RD_MAX_GROUPS)";
     case RD_EHIP: return "HIP runtime error while launching";
+    case RD_ESCRATCH: return "the call needs more device scratch than rd_forward_noalloc holds (RD_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -98,6 +100,13 @@ int rd_forward(const void* x, const void* w, const int32_t* group_sizes, int32_t
                void* stream) {
   return forward_common(x, w, group_sizes, num_groups, group_offset, num_local, limit, out, out_dtype, m,
                         k, n, workspace, workspace_bytes, stream, false);
+}
+
+int rd_forward_noalloc(const void* x, const void* w, const int32_t* group_sizes, int32_t num_groups,
+                       const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* out,
+                       int32_t out_dtype, int64_t m, int64_t k, int64_t n, void* stream) {
+  return forward_common(x, w, group_sizes, num_groups, group_offset, num_local, limit, out, out_dtype, m, k, n,
+                        nullptr, 0, stream, false, true);
 }
 
 int rd_forward_trans_rhs(const void* x, const void* w, const int32_t* group_sizes,

@@ -33,6 +33,7 @@
 //  * tiles are ordered so that consecutive logical tiles land on one XCD,
 //    which keeps a group's weight slab and rows in that XCD's L2.
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "rd_device.h"
@@ -1829,9 +1830,51 @@ void launch_decode(const KArgs& a, const GemmProblem& p, const DecodePlan& d, fl
   decode_streamk_reduce<NB><<<grid_size(chunks, 4), kThreads, 0, stream>>>(a, ws, d.seg_max, d.grid);
 }
 
+// ---------------------------------------------------------------- allocation-free forward
+
+// The decode split path's partial sums for callers that cannot allocate (a
+// HIP graph under capture, a serving loop that must not call hipMalloc): a
+// file-scope device array, one per GPU the library runs on, held until the
+// process ends.  Host code never passes the array's name to a kernel (in
+// host code it is a stand-in, not a device address): each device's address
+// comes from hipGetSymbolAddress, looked up once with that device current.
+static __device__ __align__(256) unsigned char scratch[RD_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+// This device's scratch address (looked up on the first call on the device), or null with *status set.
+void* scratch_address(int* status) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    *status = RD_EHIP;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      *status = RD_EHIP;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 DecodePlan plan_decode(const GemmProblem& p, bool trans_rhs) { return plan_decode_impl(p, trans_rhs); }
+
+int launch_forward_noalloc(const GemmProblem& p, hipStream_t stream) {
+  const DecodePlan d = plan_decode_impl(p, false);
+  if (!d.use) return launch_forward(p, false, nullptr, 0, stream);  // the tile kernels use no scratch
+  if (d.ws_bytes > RD_NOALLOC_SCRATCH_BYTES) return RD_ESCRATCH;
+  int status = RD_OK;
+  void* ptr = scratch_address(&status);
+  if (ptr == nullptr) return status;
+  return launch_forward(p, false, ptr, d.ws_bytes, stream);
+}
 
 int launch_forward(const GemmProblem& p, bool trans_rhs, void* workspace, size_t workspace_bytes,
                    hipStream_t stream) {

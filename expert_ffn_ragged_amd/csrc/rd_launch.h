@@ -36,6 +36,9 @@ DecodePlan plan_decode(const GemmProblem& p, bool trans_rhs);
 int launch_forward(const GemmProblem& p, bool trans_rhs, void* workspace, size_t workspace_bytes,
                    hipStream_t stream);
 int launch_trans(const GemmProblem& p, hipStream_t stream);
+// launch_forward (plain form) with the decode path's partial sums in the library's static device
+// scratch (RD_NOALLOC_SCRATCH_BYTES); RD_ESCRATCH when the sizes need more.
+int launch_forward_noalloc(const GemmProblem& p, hipStream_t stream);
 // fp8 (OCP E4M3) x [m, k] and w [g, n, k] (trans_rhs) or [g, k, n]; requires k % 128 == 0,
 // n % 16 == 0 and k * max(m, n) < 2^32.
 int launch_forward_fp8(const GemmProblem& p, bool trans_rhs, hipStream_t stream);

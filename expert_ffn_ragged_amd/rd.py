@@ -20,7 +20,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librd.so")
 
 ABI_VERSION = 6
-RD_OK, RD_EINVAL, RD_EUNSUPPORTED, RD_EHIP = 0, 1, 2, 3
+RD_OK, RD_EINVAL, RD_EUNSUPPORTED, RD_EHIP, RD_ESCRATCH = 0, 1, 2, 3, 4
+RD_NOALLOC_SCRATCH_BYTES = 80 << 20
 RD_BF16, RD_F32 = 0, 1
 _DTYPES = {torch.bfloat16: RD_BF16, torch.float32: RD_F32}
 
@@ -29,6 +30,7 @@ EXPORTS = (
     "rd_status_string",
     "rd_forward_workspace_size",
     "rd_forward",
+    "rd_forward_noalloc",
     "rd_forward_trans_rhs",
     "rd_forward_trans_rhs_fp8",
     "rd_forward_fp8",
@@ -72,6 +74,8 @@ def library():
     for name in ("rd_forward", "rd_forward_trans_rhs"):
         getattr(lib, name).restype = ctypes.c_int
         getattr(lib, name).argtypes = fwd
+    lib.rd_forward_noalloc.restype = ctypes.c_int
+    lib.rd_forward_noalloc.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, i32, i64, i64, i64, vp]
     lib.rd_forward_trans_rhs_fp8.restype = ctypes.c_int
     lib.rd_forward_trans_rhs_fp8.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, i32, i64, i64, i64, vp]
     lib.rd_forward_fp8.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, i32, i64, i64, i64, vp]
@@ -212,6 +216,30 @@ def ragged_dot(x, w, group_sizes, group_offset=None, limit=None, trans_rhs=False
     _check(fn(_ptr(x), _ptr(w), _ptr(group_sizes), group_sizes.numel(), _ptr(group_offset), gl,
               _ptr(limit), _ptr(out), _DTYPES[out.dtype], m, k, n,
               _ptr(workspace) if ws_bytes else None, ws_bytes, _stream(stream)))
+    return out
+
+
+def ragged_dot_noalloc(x, w, group_sizes, group_offset=None, limit=None, out=None, stream=None):
+    """ragged_dot (plain form) through rd_forward_noalloc: the library allocates nothing (the decode
+    path's partial sums live in its static per-GPU scratch); ``out`` ([m, n] bf16 or float32) should be
+    given by callers that cannot allocate.  Calls overlapping on one GPU race on that scratch."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(w, "w", torch.bfloat16, 3)
+    _need(group_sizes, "group_sizes", torch.int32, 1)
+    group_offset = _scalar(group_offset, "group_offset")
+    limit = _scalar(limit, "limit")
+    m, k = x.shape
+    gl, kw, n = w.shape
+    if kw != k:
+        raise ValueError("contraction sizes of x and w differ")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+        _on_stream(stream, out)
+    _need(out, "out", out.dtype, 2)
+    if tuple(out.shape) != (m, n) or out.dtype not in _DTYPES:
+        raise ValueError("out must be [m, n] bf16 or float32")
+    _check(library().rd_forward_noalloc(_ptr(x), _ptr(w), _ptr(group_sizes), group_sizes.numel(), _ptr(group_offset),
+                                        gl, _ptr(limit), _ptr(out), _DTYPES[out.dtype], m, k, n, _stream(stream)))
     return out
 
 

@@ -58,6 +58,7 @@ extern "C" {
 #define RD_EINVAL 1        /* a host-visible argument is invalid           */
 #define RD_EUNSUPPORTED 2  /* valid but outside what the kernels support   */
 #define RD_EHIP 3          /* the HIP runtime reported an error            */
+#define RD_ESCRATCH 4      /* rd_forward_noalloc: sizes need more scratch  */
 
 /* element types */
 #define RD_BF16 0
@@ -119,6 +120,29 @@ int rd_forward(const void* x, const void* w, const int32_t* group_sizes, int32_t
                const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* out,
                int32_t out_dtype, int64_t m, int64_t k, int64_t n, void* workspace, size_t workspace_bytes,
                void* stream);
+
+/*
+ * rd_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same computation and results as rd_forward with a workspace of
+ * rd_forward_workspace_size(m, k, n, num_local, 0) bytes, but the
+ * split-contraction decode path keeps its fp32 partial sums in a static
+ * device array of RD_NOALLOC_SCRATCH_BYTES per GPU, reserved when the library
+ * is loaded and held until the process ends; no call allocates or frees
+ * anything.  Calls whose sizes need more scratch than that return
+ * RD_ESCRATCH before anything is launched (the 64-token top-8 decode step
+ * over 128 experts of k 4096, n 1536 needs 72 MiB on a 256-CU device).
+ * Every call on a GPU uses that GPU's one array, whose contents are left
+ * over from the last call (every location a call reads it has written
+ * first): calls that overlap on one GPU, from several streams or threads,
+ * race and must be serialised by the caller.  The first call on a device
+ * looks the array's address up (not inside a graph capture: make one call
+ * on the device before capturing).
+ */
+#define RD_NOALLOC_SCRATCH_BYTES (80u << 20)
+int rd_forward_noalloc(const void* x, const void* w, const int32_t* group_sizes, int32_t num_groups,
+                       const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* out,
+                       int32_t out_dtype, int64_t m, int64_t k, int64_t n, void* stream);
 
 /*
  * ragged_dot with trans_rhs ([SkyRL], the dx rule of the backward):

@@ -181,3 +181,16 @@ def test_tuning_hook_validates_and_restores(lib):
             pass
     # the built-in choices are back (no effect is observable without a GPU; the calls succeed)
     assert lib.rd_tune_set(rd.RD_TUNE_FWD_TILE, -1) == rd.RD_OK
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch_before_launching(lib):
+    # 4096 rows over 256 experts (16 rows each on average), k 4096, n 1536: the decode split path's
+    # partial sums need about 96 MiB on a 256-CU device, more than the 80 MiB static scratch
+    need = lib.rd_forward_workspace_size(4096, 4096, 1536, 256, 0)
+    assert need > rd.RD_NOALLOC_SCRATCH_BYTES
+    v = ctypes.c_void_p
+    st = lib.rd_forward_noalloc(v(16), v(16), v(16), 256, None, 256, None, v(16), 0, 4096, 4096, 1536, None)
+    assert st == rd.RD_ESCRATCH
+    assert b"scratch" in lib.rd_status_string(st)
+    # the decode step of 64 tokens x top-8 over 128 experts fits
+    assert 0 < lib.rd_forward_workspace_size(512, 4096, 1536, 128, 0) <= rd.RD_NOALLOC_SCRATCH_BYTES
