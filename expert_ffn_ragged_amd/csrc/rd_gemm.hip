@@ -706,6 +706,18 @@ struct FwdTiles {
   }
 };
 
+// The slots a workgroup walks, in order: base, base + step, ... (count of them).
+struct SlotSeq {
+  long long base, step, count;
+  __device__ __forceinline__ long long at(long long u) const { return base + u * step; }
+};
+
+// Every gridDim.x-th slot from blockIdx.x (the forward tiles all cost the same).
+__device__ __forceinline__ SlotSeq strided_slots(long long slots) {
+  const long long b = blockIdx.x, g = gridDim.x;
+  return SlotSeq{b, g, b < slots ? (slots - b + g - 1) / g : 0};
+}
+
 // trans_ragged_dot tiles: every local group owns ka x nc output tiles of
 // dW[j]; the contraction runs over the group's rows.  Groups are visited
 // largest first (s_order).  The eight XCDs form an xa x xc grid: XCD
@@ -763,6 +775,54 @@ struct TransTiles {
     t.c0 = ct * BN;
     t.nk = (t.r_end - t.r_begin + KS - 1) / KS;
     return true;
+  }
+
+  // Which slots this workgroup takes.  A tile costs its group's contraction
+  // steps.  Dealt round-robin over a largest-first list (slot s to workgroup
+  // s mod gridDim.x), every workgroup that takes one of the largest groups'
+  // tiles also takes its full share of the later ones: with Zipf-sized groups
+  // on the 32768-row backward the busiest workgroup has 450 steps against 264
+  // on average.  So tiles costing at least the mean work per workgroup (the
+  // "heavy" tiles, a prefix of the list) get a workgroup each, and the other
+  // workgroups deal the remaining slots round-robin among themselves (busiest
+  // 298 there, the cost of one heavy tile).  Workgroups keep walking the list
+  // together, so the ones running at the same time work on neighbouring
+  // tiles that share their rows in L2 (contiguous per-workgroup ranges, also
+  // tried, lose that and are 30 % slower).  NT threads; uses s_wave; ends
+  // with a barrier.
+  template <int NT, int KS>
+  __device__ SlotSeq dealt_slots(const int* s_lb, const int* s_order, int gl, long long* s_wave) const {
+    const long long tpg = static_cast<long long>(kax) * ncx * (split ? kXcds : 1);  // slots of one group
+    const long long G = gridDim.x;
+    auto steps_of = [&](int q) {
+      const int j = s_order[q];
+      const long long st = (s_lb[j + 1] - s_lb[j] + KS - 1) / KS;
+      return st < 1 ? 1ll : st;
+    };
+    auto block_sum = [&](long long v) {
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+      __syncthreads();
+      if ((threadIdx.x & 63) == 0) s_wave[threadIdx.x >> 6] = v;
+      __syncthreads();
+      long long sum = 0;
+      for (int w = 0; w < NT / 64; ++w) sum += s_wave[w];
+      return sum;
+    };
+    long long mine = 0;
+    for (int q = threadIdx.x; q < gl; q += NT) mine += tpg * steps_of(q);
+    const long long total = block_sum(mine);
+    long long heavy = 0;
+    for (int q = threadIdx.x; q < gl; q += NT) heavy += steps_of(q) * G >= total ? 1 : 0;
+    heavy = block_sum(heavy);
+    __syncthreads();  // s_wave is reused next
+    long long H = heavy * tpg;
+    if (H > G - 1) H = G - 1;
+    const long long b = blockIdx.x;
+    if (H <= 0 || slots <= G) return strided_slots(slots);
+    if (b < H) return SlotSeq{b, 1, 1};
+    const long long step = G - H;
+    return SlotSeq{b, step, b < slots ? (slots - b + step - 1) / step : 0};
   }
 };
 
@@ -1128,10 +1188,14 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
       return tl.template get<BM, TN, KS>(s, s_lb, s_aux, p.gl, p.k, t);
   };
   const uint32_t ring = lds_address(s_tiles);
-  const long long stride = gridDim.x;
+  SlotSeq seq;
+  if constexpr (is_trans(MODE))
+    seq = tl.template dealt_slots<NT, KSTEP>(s_lb, s_aux, p.gl, s_wave);
+  else
+    seq = strided_slots(tl.slots);
 
   // producer state: its tile (slot ps), operands, next step
-  long long ps = static_cast<long long>(blockIdx.x) - stride;
+  long long pu = -1;  // producer: index into seq of its current tile
   int p_kt = 0, p_nk = 0;
   bool p_done = false;
   OpA pa;
@@ -1139,13 +1203,12 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
   int issued = 0;
   auto produce = [&]() {
     while (!p_done && p_kt >= p_nk) {
-      ps += stride;
-      if (ps >= tl.slots) {
+      if (++pu >= seq.count) {
         p_done = true;
         break;
       }
       typename Tiles::Tile t;
-      if (tile_at(ps, t) && t.nk > 0) {
+      if (tile_at(seq.at(pu), t) && t.nk > 0) {
         Ops::make(p, t, wave, pa, pb);
         p_kt = 0;
         p_nk = t.nk;
@@ -1163,9 +1226,9 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
   for (int i = 0; i < S - 1; ++i) produce();
 
   int g = 0;  // consumer step
-  for (long long cs = blockIdx.x; cs < tl.slots; cs += stride) {
+  for (long long u = 0; u < seq.count; ++u) {
     typename Tiles::Tile t;
-    if (!tile_at(cs, t)) continue;
+    if (!tile_at(seq.at(u), t)) continue;
     char* out;
     int r0, rlim, c0;
     if constexpr (is_trans(MODE)) {
@@ -1304,10 +1367,14 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_pp(KArgs p) {
       return tl.template get<BM, BN, KS>(s, s_lb, s_aux, p.gl, p.k, t);
   };
   const uint32_t ring = lds_address(s_tiles);
-  const long long stride = gridDim.x;
+  SlotSeq seq;
+  if constexpr (is_trans(MODE))
+    seq = tl.template dealt_slots<NT, KS>(s_lb, s_aux, p.gl, s_wave);
+  else
+    seq = strided_slots(tl.slots);
 
   // producer: this wave's share of every stage, walking the tile list ahead of the consumer
-  long long ps = static_cast<long long>(blockIdx.x) - stride;
+  long long pu = -1;  // producer: index into seq of its current tile
   int p_kt = 0, p_nk = 0;
   bool p_done = false;
   OpA pa;
@@ -1315,13 +1382,12 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_pp(KArgs p) {
   int issued = 0;
   auto produce = [&]() {
     while (!p_done && p_kt >= p_nk) {
-      ps += stride;
-      if (ps >= tl.slots) {
+      if (++pu >= seq.count) {
         p_done = true;
         break;
       }
       typename Tiles::Tile t;
-      if (tile_at(ps, t) && t.nk > 0) {
+      if (tile_at(seq.at(pu), t) && t.nk > 0) {
         Ops::make(p, t, wave, pa, pb);
         p_kt = 0;
         p_nk = t.nk;
@@ -1348,9 +1414,9 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_pp(KArgs p) {
   if (grp == 1) barrier();  // group B runs one phase behind
 
   int g = 0;  // consumer stage
-  for (long long cs = blockIdx.x; cs < tl.slots; cs += stride) {
+  for (long long u = 0; u < seq.count; ++u) {
     typename Tiles::Tile t;
-    if (!tile_at(cs, t)) continue;
+    if (!tile_at(seq.at(u), t)) continue;
     char* out;
     int r0, rlim, c0;
     if constexpr (is_trans(MODE)) {
