@@ -47,6 +47,10 @@ def parse():
                     help="only the headline step (for profiler runs), no extra workloads")
     ap.add_argument("--sweep", action="store_true",
                     help="time every tile shape of every grouped GEMM on the workloads and print the table")
+    ap.add_argument("--profile", choices=("backward", "upproj", "decode", "packed"),
+                    help="only run one workload's kernels, --warmup + --steps times each, for a profiler")
+    ap.add_argument("--cold", action="store_true",
+                    help="with --profile: flush L2 and the MALL (a 512 MiB write) before every pass")
     ap.add_argument("--copy-calib", action="store_true",
                     help="first copy 256 MiB device-to-device three times (reference kernel for HBM counters)")
     ap.add_argument("--api-region", action="store_true",
@@ -170,6 +174,8 @@ def upproj(steps, warmup):
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "upproj_fwd_bwd_traffic.md")
 BACKWARD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "backward_m32768_traffic.md")
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_m512_traffic.md")
+PACKED_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "packed_buffer_limit126156_traffic.md")
 
 
 def measured_traffic(path=TRAFFIC_FILE):
@@ -263,7 +269,7 @@ def extra_workloads(steps, warmup):
     rows = int(d["gs_host"].sum())
     # algorithmic bytes: x rows, the weights of non-empty experts, the output
     nb = rows * d["k"] * 2 + int(nz.sum()) * d["k"] * d["n"] * 2 + rows * d["n"] * 2
-    tr = measured_traffic()
+    tr = measured_traffic(DECODE_TRAFFIC_FILE)
     t = (tr["decode_gemm"] + tr.get("decode_reduce", 0.0)) if "decode_gemm" in tr else None
     out["decode_m512_k4096_n1536_g128"] = {
         "ms": round(per["decode"], 4), "GB/s": round(nb / per["decode"] / 1e6, 1),
@@ -337,9 +343,12 @@ def extra_all(steps):
     ms = per["window_ragged_dot"]
     out["window_limit_ragged_dot"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1),
                                       "GB/s": round(nb / ms / 1e6, 1)}
+    tr = measured_traffic(PACKED_TRAFFIC_FILE)
     for key, nbytes in (("glu_fwd", L * h * 6), ("glu_bwd", L * h * 10)):
         out[f"window_limit_{key}"] = {"ms": round(per[key], 4), "GB/s": round(nbytes / per[key] / 1e6, 1),
-                                      "hbm_frac": round(nbytes / per[key] / 1e6 / HBM_PEAK_GBS, 4)}
+                                      "hbm_frac": round(nbytes / per[key] / 1e6 / HBM_PEAK_GBS, 4),
+                                      "algorithmic_bytes": int(nbytes),
+                                      "traffic": None if key not in tr else int(tr[key])}
     del d, o, g, gb
     torch.cuda.empty_cache()
     # weighted unsort backward over the packed buffer's valid rows
@@ -352,7 +361,8 @@ def extra_all(steps):
     nbytes = L * (3 * hid * 2 + 8)  # g, y read, grad written (bf16); w read, dot written (f32)
     out["window_limit_unsort_bwd_rows"] = {"ms": round(per["unsort"], 4), "GB/s": round(nbytes / per["unsort"] / 1e6, 1),
                                            "hbm_frac": round(nbytes / per["unsort"] / 1e6 / HBM_PEAK_GBS, 4),
-                                           "algorithmic_bytes": int(nbytes)}
+                                           "algorithmic_bytes": int(nbytes),
+                                           "traffic": None if "unsort_bwd_rows" not in tr else int(tr["unsort_bwd_rows"])}
     del d, grad, dot
     torch.cuda.empty_cache()
     out.update(mlp_layer(steps))
@@ -542,13 +552,23 @@ def cpu_baseline(x, w, dy, gs_host, budget_s=15.0):
 
 
 def sweep(steps):
-    """Every tile shape of every grouped GEMM on the workloads: one JSON line per (op, tile) with its mean
-    time, then one summary line per op with the built-in choice and the fastest shape."""
+    """Every tile shape of every grouped GEMM on the five workloads: one JSON line per (op, tile) with its
+    mean time, one summary line per op (the built-in choice and the fastest shape), then the whole table
+    as Markdown (ms; "default" is the built-in choice from m, k, n and num_local)."""
     import torch
 
     from expert_ffn_ragged_amd import rd, workloads
 
     cases = []
+    d1 = workloads.make(1, "cuda")
+    w1t = d1["w"].transpose(1, 2).contiguous()
+    o1 = torch.empty((d1["m"], d1["n"]), dtype=torch.bfloat16, device="cuda")
+    o1t = torch.empty((d1["m"], d1["k"]), dtype=torch.bfloat16, device="cuda")
+    dw1 = torch.empty((4, d1["k"], d1["n"]), dtype=torch.bfloat16, device="cuda")
+    cases += [("tiny_ragged_dot", "fwd", lambda: rd.ragged_dot(d1["x"], d1["w"], d1["gs"], out=o1)),
+              ("tiny_trans_rhs", "fwd", lambda: rd.ragged_dot(d1["dy"], d1["w"], d1["gs"], trans_rhs=True, out=o1t)),
+              ("tiny_trans_ragged_dot", "trans", lambda: rd.trans_ragged_dot(d1["x"], d1["dy"], d1["gs"], out=dw1))]
+    del w1t
     d2 = workloads.make(2, "cuda", parts=("x", "w", "dy"))
     m2, k2, n2 = d2["m"], d2["k"], d2["n"]
     o2 = torch.empty((m2, n2), dtype=torch.bfloat16, device="cuda")
@@ -568,13 +588,25 @@ def sweep(steps):
                lambda: rd.ragged_dot(d3["dy"], d3["w"], d3["gs"], trans_rhs=True, out=dx3)),
               ("backward_dw_trans_ragged_dot", "trans", lambda: rd.trans_ragged_dot(d3["x"], d3["dy"], d3["gs"],
                                                                                       out=dw3))]
+    d4 = workloads.make(4, "cuda", parts=("x", "w"))
+    off4 = torch.tensor([96], dtype=torch.int32, device="cuda")
+    lim4 = torch.tensor([d4["limit"]], dtype=torch.int32, device="cuda")
+    o4 = torch.empty((d4["m"], d4["n"]), dtype=torch.bfloat16, device="cuda")
+    cases += [("window_limit_ragged_dot", "fwd", lambda: rd.ragged_dot(d4["x"], d4["w"], d4["gs"], off4, lim4,
+                                                                       out=o4))]
     d5 = workloads.make(5, "cuda", parts=("x", "w"))
     o5 = torch.empty((d5["m"], d5["n"]), dtype=torch.bfloat16, device="cuda")
     cases += [("decode_ragged_dot_tile_path", "fwd", lambda: rd.ragged_dot(d5["x"], d5["w"], d5["gs"], out=o5))]
     ntile = rd.tile_count()
+    with rd.tuning(decode=False):  # warm every case (and the clocks) before timing any
+        for _ in range(3):
+            for _, _, fn in cases:
+                fn()
+        torch.cuda.synchronize()
+    table = {}
     for name, kind, fn in cases:
         times = {}
-        for tile in [None] + list(range(ntile)):
+        for tile in list(range(ntile)) + [None]:
             kw = {"fwd_tile" if kind == "fwd" else "trans_tile": tile, "decode": False}
             with rd.tuning(**kw):
                 _, _, per = timed_ops([(name, fn)], steps, 2)
@@ -584,8 +616,67 @@ def sweep(steps):
         best = min((t for t in times if t != "default"), key=lambda t: times[t])
         print(json.dumps({"sweep_summary": name, "default_ms": round(times["default"], 4), "best_tile": best,
                           "best_ms": round(times[best], 4)}), flush=True)
-    del d2, d3, d5
+        table[name] = times
+    print("| op | default | " + " | ".join(str(t) for t in range(ntile)) + " |")
+    print("|---|---|" + "---|" * ntile)
+    for name, times in table.items():
+        best = min(times.values())
+        cell = lambda v: f"**{v:.3f}**" if v == best else f"{v:.3f}"
+        print(f"| {name} | {cell(times['default'])} | " + " | ".join(cell(times[t]) for t in range(ntile)) + " |")
+    del d1, d2, d3, d4, d5
     torch.cuda.empty_cache()
+
+
+def profile_run(which, steps, warmup, cold=False):
+    """One workload's kernels and nothing else (no timing, no oracle), for rocprofv3 runs; with cold, the
+    caches are flushed before every pass as in the headline's timing."""
+    import torch
+
+    from expert_ffn_ragged_amd import rd, workloads
+
+    ops = []
+    if which == "backward":
+        d = workloads.make(3, "cuda")
+        dx = torch.empty((d["m"], d["k"]), dtype=torch.bfloat16, device="cuda")
+        dw = torch.empty((d["G"], d["k"], d["n"]), dtype=torch.bfloat16, device="cuda")
+        ops = [lambda: rd.ragged_dot(d["dy"], d["w"], d["gs"], trans_rhs=True, out=dx),
+               lambda: rd.trans_ragged_dot(d["x"], d["dy"], d["gs"], out=dw)]
+    elif which == "upproj":
+        d = workloads.make(2, "cuda", parts=("x", "w"))
+        m, k, n = d["m"], d["k"], d["n"]
+        x, w, gs = d["x"], d["w"], d["gs"]
+        d_act = workloads.bf16_normal((m, n // 2), 1.0, 2006, "cuda")
+        fused = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        act = torch.empty((m, n // 2), dtype=torch.bfloat16, device="cuda")
+        dfused = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        dx = torch.empty((m, k), dtype=torch.bfloat16, device="cuda")
+        dw = torch.empty((w.shape[0], k, n), dtype=torch.bfloat16, device="cuda")
+        ops = [lambda: rd.ragged_dot(x, w, gs, out=fused), lambda: rd.glu_fwd(fused, out=act),
+               lambda: rd.glu_bwd(fused, d_act, out=dfused),
+               lambda: rd.ragged_dot(dfused, w, gs, trans_rhs=True, out=dx),
+               lambda: rd.trans_ragged_dot(x, dfused, gs, out=dw)]
+    elif which == "decode":
+        d = workloads.make(5, "cuda", parts=("x", "w"))
+        o = torch.empty((d["m"], d["n"]), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(max(rd.library().rd_forward_workspace_size(d["m"], d["k"], d["n"], d["G"], 0), 16),
+                         dtype=torch.uint8, device="cuda")
+        ops = [lambda: rd.ragged_dot(d["x"], d["w"], d["gs"], out=o, workspace=ws)]
+    else:  # the packed expert buffer: GLU forward / backward and the unsort backward at limit 126156
+        d = workloads.make(4, "cuda", parts=("fused", "d_out", "ug", "uy", "uw"))
+        lim = torch.tensor([d["limit"]], dtype=torch.int32, device="cuda")
+        g = torch.empty((d["m"], d["n"]), dtype=torch.bfloat16, device="cuda")
+        gb = torch.empty((d["m"], 2 * d["n"]), dtype=torch.bfloat16, device="cuda")
+        grad = torch.empty((d["m"], d["k"]), dtype=torch.bfloat16, device="cuda")
+        dot = torch.empty((d["m"],), dtype=torch.float32, device="cuda")
+        ops = [lambda: rd.glu_fwd(d["fused"], lim, out=g), lambda: rd.glu_bwd(d["fused"], d["d_out"], lim, out=gb),
+               lambda: rd.unsort_bwd_rows(d["ug"], d["uy"], d["uw"], lim, grad=grad, dot=dot)]
+    for _ in range(warmup + steps):
+        if cold:
+            flush_caches()
+        for fn in ops:
+            fn()
+    torch.cuda.synchronize()
+    print(json.dumps({"profile": which, "launches_per_op": warmup + steps, "cold": cold}), flush=True)
 
 
 def main():
@@ -608,6 +699,16 @@ def main():
         return
     if args.sweep:
         sweep(max(args.steps, 5))
+        return
+    if args.profile:
+        if args.copy_calib:
+            a = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+            b = torch.empty_like(a)
+            for _ in range(3):
+                b.copy_(a)
+            torch.cuda.synchronize()
+            del a, b
+        profile_run(args.profile, args.steps, args.warmup, args.cold)
         return
     if args.copy_calib:
         a = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")

@@ -150,19 +150,41 @@ def traffic_summary(fetch_dir, write_dir, mfma_dir, command, title=DEFAULT_TITLE
     return "\n".join(lines) + "\n"
 
 
-def stats_summary(stats_dir, command, title):
+def steady_durations(stats_dir, skip):
+    """{kernel short name: [durations in us]} from the kernel trace, dropping each kernel's first `skip`
+    dispatches (the warm-up launches of the profiled command)."""
+    per = {}
+    for row in sorted(_rows(stats_dir, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"])):
+        if op_of(row["Kernel_Name"]) is None:
+            continue
+        per.setdefault(short_name(row["Kernel_Name"]), []).append(
+            (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3)
+    return {k: v[skip:] for k, v in per.items() if len(v) > skip}
+
+
+def stats_summary(stats_dir, command, title, skip=0):
     rows = []
     for row in _rows(stats_dir, "kernel_stats.csv"):
         if op_of(row["Name"]) is None:
             continue
         rows.append((short_name(row["Name"]), int(row["Calls"]), float(row["AverageNs"]) / 1e3,
                      float(row["MinNs"]) / 1e3, float(row["MaxNs"]) / 1e3))
+    steady = steady_durations(stats_dir, skip) if skip else {}
     lines = [f"# Kernel durations: {title}", "", "Command (run from the repository root on the GPU box "
              "with `TMPDIR=/tmp` exported):", "", "```", command, "```", "",
-             f"source digest: {source_digest()}", "",
-             "| kernel | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
+             f"source digest: {source_digest()}", ""]
+    if skip:
+        lines += [f"The last two columns leave out each kernel's first {skip} dispatches (the command's warm-up "
+                  "launches), from the kernel trace of the same run.", ""]
+    lines += ["| kernel | calls | average (us) | min (us) | max (us) |" + (" timed calls | timed average (us) |"
+                                                                          if skip else ""),
+              "|---|---|---|---|---|" + ("---|---|" if skip else "")]
     for name, calls, avg, mn, mx in sorted(rows, key=lambda r: -r[2]):
-        lines.append(f"| `{name}` | {calls} | {avg:.1f} | {mn:.1f} | {mx:.1f} |")
+        extra = ""
+        if skip:
+            d = steady.get(name, [])
+            extra = f" {len(d)} | {sum(d) / len(d):.1f} |" if d else " 0 | - |"
+        lines.append(f"| `{name}` | {calls} | {avg:.1f} | {mn:.1f} | {mx:.1f} |" + extra)
     return "\n".join(lines) + "\n"
 
 
@@ -295,6 +317,7 @@ def main():
     s.add_argument("--stats", required=True)
     s.add_argument("--command", required=True)
     s.add_argument("--title", required=True)
+    s.add_argument("--skip", type=int, default=0, help="leave out each kernel's first N dispatches")
     s.add_argument("--out", required=True)
     lp = sub.add_parser("loadpath")
     lp.add_argument("--dirs", nargs="+", required=True)
@@ -313,7 +336,7 @@ def main():
     elif a.what == "apitrace":
         text = apitrace_summary(a.trace, a.command)
     else:
-        text = stats_summary(a.stats, a.command, a.title)
+        text = stats_summary(a.stats, a.command, a.title, a.skip)
     with open(a.out, "w") as fh:
         fh.write(text)
     print(text)
