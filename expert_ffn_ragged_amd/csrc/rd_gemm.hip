@@ -1752,9 +1752,11 @@ int grid_size(long long work_items, int per_cu) {
   return static_cast<int>(g < 1 ? 1 : g);
 }
 
-// Tile shapes (BM x BN, LDS stages) of the buffer-to-LDS pipeline.  Every
-// shape runs 4 waves in a 2 x 2 layout; larger wave tiles read fewer LDS bytes
-// per MFMA, smaller BM wastes fewer MFMA rows on short groups.
+// Tile shapes (BM x BN, LDS stages) of the buffer-to-LDS pipeline.  kT shapes
+// run 4 waves in a 2 x 2 layout (the x2 / x3 ones two or three workgroups per
+// CU), kW shapes 8 waves sharing one ring, kP the ping-pong kernel; larger
+// wave tiles read fewer LDS bytes per MFMA, smaller BM wastes fewer MFMA rows
+// on short groups.
 enum Tile { kT64x128 = 0, kT128x128 = 1, kT128x256 = 2, kT256x256 = 3, kT128x128x2 = 4, kT64x64 = 5, kT256x256k32 = 6,
             kT128x256k32 = 7, kT128x256x2 = 8, kT128x128k32x2 = 9, kT128x128x3 = 10, kT256x128x2 = 11,
             kT128x256s3x2 = 12, kW256x256 = 13, kW128x256 = 14, kW256x256k64 = 15, kW128x512 = 16, kW128x256k32 = 17, kP256x256 = 18, kTileCount };
