@@ -304,6 +304,16 @@ def extra_all(steps):
     for key, ms in per.items():
         out[f"backward_m32768_{key}"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1),
                                         "mfma_frac": round(fl / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    # one hot expert (60 % of the rows) at the same shape: trans_ragged_dot with the row split of long
+    # groups (the default) and without it
+    gsh = torch.tensor(workloads.hot_expert_sizes(), dtype=torch.int32, device="cuda")
+    _, _, per_h = timed_ops([
+        ("split", lambda: rd.trans_ragged_dot(d["x"], d["dy"], gsh, out=dw)),
+        ("unsplit", lambda: rd.trans_ragged_dot(d["x"], d["dy"], gsh, out=dw, row_split=False)),
+    ], steps, 3)
+    out["backward_m32768_hot_expert_dw"] = {
+        key: {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1)} for key, ms in per_h.items()}
+    out["backward_m32768_hot_expert_dw"]["sizes"] = "19660 rows in one expert, the rest Zipf(1.1) over 63"
     fld = 2.0 * m * k * n
     out["backward_m32768_dx_dense_torch_reference"] = {
         "ms": round(per_d["dense"], 4), "TFLOP/s": round(fld / per_d["dense"] / 1e9, 1),

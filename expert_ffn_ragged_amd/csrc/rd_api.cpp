@@ -199,11 +199,13 @@ int rd_forward_trans_rhs_fp8(const void* x, const void* w, const int32_t* group_
 }
 
 size_t rd_trans_workspace_size(int64_t m, int64_t k, int64_t n, int32_t num_local) {
-  (void)m;
-  (void)k;
-  (void)n;
-  (void)num_local;
-  return 0;  // every dw tile is reduced by one workgroup: no partials to stage
+  if (check_dims(m, k, n) != RD_OK || num_local <= 0 || num_local > RD_MAX_GROUPS || m == 0) return 0;
+  rd::GemmProblem p{};
+  p.num_local = num_local;
+  p.m = static_cast<int>(m);
+  p.k = static_cast<int>(k);
+  p.n = static_cast<int>(n);
+  return rd::trans_workspace_size(p);
 }
 
 int rd_trans_fp8(const void* x, const void* dy, const int32_t* group_sizes, int32_t num_groups,
@@ -242,8 +244,6 @@ int rd_trans(const void* x, const void* dy, const int32_t* group_sizes, int32_t 
              const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* dw,
              int32_t dw_dtype, int64_t m, int64_t k, int64_t n, void* workspace,
              size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   int st = check_dims(m, k, n);
   if (st != RD_OK) return st;
   st = check_groups(num_groups, group_offset, num_local);
@@ -254,6 +254,7 @@ int rd_trans(const void* x, const void* dy, const int32_t* group_sizes, int32_t 
   if ((m > 0 && (!aligned16(x) || !aligned16(dy))) || !aligned16(dw)) return RD_EINVAL;
   if ((reinterpret_cast<uintptr_t>(group_sizes) & 3u) || (reinterpret_cast<uintptr_t>(limit) & 3u))
     return RD_EINVAL;
+  if (workspace_bytes > 0 && (workspace == nullptr || !aligned16(workspace))) return RD_EINVAL;
   rd::GemmProblem p{};
   p.a = x;
   p.b = dy;
@@ -267,7 +268,8 @@ int rd_trans(const void* x, const void* dy, const int32_t* group_sizes, int32_t 
   p.m = static_cast<int>(m);
   p.k = static_cast<int>(k);
   p.n = static_cast<int>(n);
-  return rd::launch_trans(p, static_cast<hipStream_t>(stream));
+  return rd::launch_trans(p, workspace_bytes > 0 ? workspace : nullptr, workspace_bytes,
+                          static_cast<hipStream_t>(stream));
 }
 
 int rd_glu_fwd(const void* fused, const int32_t* limit, void* out, int64_t rows, int64_t h,

@@ -58,6 +58,9 @@ struct KArgs {
   const int32_t* limp;
   void* out;
   void* out2;  // kFwdGLU: the [gate | up] buffer [m, 2n] (may be null); out is silu(gate) * up [m, n]
+  void* ws;    // kTransTN: row-split workspace (header, then fp32 partial tiles), or null
+  long long ws_bytes;
+  int per_cu;  // workgroups of this launch sharing a CU (ceil(grid / CUs))
   int G, gl, out_f32;
   int m, k, n;
 };
@@ -706,16 +709,33 @@ struct FwdTiles {
   }
 };
 
-// The slots a workgroup walks, in order: base, base + step, ... (count of them).
+// The slots a workgroup walks: round u takes slot origin + u * step + pos,
+// pos = p, or step - 1 - p on odd rounds when snake is set (count of them).
 struct SlotSeq {
-  long long base, step, count;
-  __device__ __forceinline__ long long at(long long u) const { return base + u * step; }
+  long long origin, step, count;
+  long long p;
+  bool snake;
+  __device__ __forceinline__ long long at(long long u) const {
+    return origin + u * step + ((snake && (u & 1)) ? step - 1 - p : p);
+  }
 };
 
 // Every gridDim.x-th slot from blockIdx.x (the forward tiles all cost the same).
 __device__ __forceinline__ SlotSeq strided_slots(long long slots) {
   const long long b = blockIdx.x, g = gridDim.x;
-  return SlotSeq{b, g, b < slots ? (slots - b + g - 1) / g : 0};
+  return SlotSeq{0, g, b < slots ? (slots - b + g - 1) / g : 0, b, false};
+}
+
+// Position p of `step` in every round of slots [origin, end), the order
+// reversed on odd rounds: the slots of a list sorted by falling cost even out
+// over the positions (round-robin gives the first positions the dearest slot
+// of every round).
+__device__ __forceinline__ SlotSeq snake_slots(long long origin, long long end, long long step, long long p) {
+  const long long n = end - origin;
+  if (n <= 0 || step <= 0) return SlotSeq{origin, 1, 0, 0, false};
+  const long long rounds = n / step, rem = n % step;
+  const long long last = (rounds & 1) ? step - 1 - p : p;  // position taken in the partial round
+  return SlotSeq{origin, step, rounds + (last < rem ? 1 : 0), p, true};
 }
 
 // trans_ragged_dot tiles: every local group owns ka x nc output tiles of
@@ -725,12 +745,31 @@ __device__ __forceinline__ SlotSeq strided_slots(long long slots) {
 // every group, so each XCD does an equal share of every group and a row block
 // of x (dy) is fetched by xc (xa) XCDs.  The grid shape minimises that
 // re-read traffic, k * xc + n * xa.
+//
+// Row split (plan(), with a caller workspace): a group whose contraction
+// costs at least the mean work per CU, and more than one chunk, is cut into P
+// row chunks of equal step counts, so that no tile holds up the grid.
+// Those groups are a prefix of the largest-first order (at most kMaxSplit of
+// them).  A chunk's tile is written as an fp32 partial to the workspace; a
+// second kernel (trans_split_reduce) adds a tile's P partials in chunk order,
+// so the result does not depend on scheduling.  The list holds, in order,
+// every chunk of the split groups (chunk-major: the tiles of one chunk share
+// its rows), then every other group.  Without the split (no workspace, or
+// kernels that do not call plan()) the list is as before, one unit per group.
+constexpr int kMaxSplit = 16;
+// workspace header: [0] ns, [1] BM, [2] BN, then (j, P, first chunk) per split group from [3]
+constexpr int kSplitHeaderInts = 64;
+constexpr int kSplitMinSteps = 32;  // shortest chunk, in contraction steps
+static_assert(3 + 3 * kMaxSplit <= kSplitHeaderInts, "split header");
+
 struct TransTiles {
-  long long per_x, slots;
+  long long tpg, slots;  // slots per list unit (a group, or a chunk of a split group), slots
   int ka, nc, kax, ncx, xc;
-  bool split;
+  bool split;            // the XCD grid
+  int ns, cs;            // split groups, chunk length bound (steps)
   struct Tile {
     int j, r_begin, r_end, a0, c0, nk;
+    int part;  // partial tile index in the workspace, or -1: write dW directly
   };
   __device__ __forceinline__ void init(int gl, int k, int n, int BM, int BN) {
     ka = (k + BM - 1) / BM;
@@ -752,77 +791,154 @@ struct TransTiles {
     if (!split) xa = xc = 1;
     kax = (ka + xa - 1) / xa;
     ncx = (nc + xc - 1) / xc;
-    per_x = static_cast<long long>(gl) * kax * ncx;
-    slots = split ? per_x * kXcds : per_x;
+    tpg = static_cast<long long>(kax) * ncx * (split ? kXcds : 1);
+    slots = static_cast<long long>(gl) * tpg;
+    ns = 0;
+    cs = 0;
   }
-  template <int BM, int BN, int KS = BK>
-  __device__ __forceinline__ bool get(long long s, const int* s_lb, const int* s_order, Tile& t) const {
-    int x = 0;
-    long long i = s;
-    if (split) {
-      x = static_cast<int>(s % kXcds);
-      i = s / kXcds;
+
+  // Contraction steps of the group at position q of s_order (at least 1: an
+  // empty group's tile still costs its zero store).
+  template <int KS>
+  __device__ __forceinline__ static long long steps_at(const int* s_lb, const int* s_order, int q) {
+    const int j = s_order[q];
+    const long long st = (s_lb[j + 1] - s_lb[j] + KS - 1) / KS;
+    return st < 1 ? 1ll : st;
+  }
+
+  // Sum of v over the workgroup's NT threads (uses s_wave; ends with a barrier).
+  template <int NT>
+  __device__ __forceinline__ static long long block_sum(long long v, long long* s_wave) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) s_wave[threadIdx.x >> 6] = v;
+    __syncthreads();
+    long long sum = 0;
+    for (int w = 0; w < NT / 64; ++w) sum += s_wave[w];
+    __syncthreads();
+    return sum;
+  }
+
+  // The row split plan, the same in every workgroup (it depends on the group
+  // sizes, the grid, per_cu and cap_tiles only): ns groups and s_cp[i] =
+  // chunks of the first i split groups (s_cp[0..ns]).  A group is split when
+  // one of its tiles costs at least the mean work per CU (per_cu workgroups
+  // share a CU): below that, the CU holding it also runs lighter work of its
+  // co-resident workgroups, and the partials' round trip through memory costs
+  // more than the balance gains (measured on the 32768-row backward, whose
+  // largest expert is 0.57 of that mean: 362 us unsplit, 386 us split).  At
+  // most cap_tiles partial tiles (the workspace); fewer split groups when
+  // they would not fit.  Workgroup 0 writes the plan to the workspace header
+  // for the reduction.  NT threads; ends with a barrier.
+  template <int NT, int KS>
+  __device__ void plan(const int* s_lb, const int* s_order, int gl, long long* s_wave, int* s_cp, long long cap_tiles,
+                       int per_cu, int* header) {
+    long long mine = 0;
+    for (int q = threadIdx.x; q < gl; q += NT) mine += steps_at<KS>(s_lb, s_order, q);
+    const long long total = block_sum<NT>(mine, s_wave) * tpg;
+    const long long G = gridDim.x;
+    long long c = (total + 2 * G - 1) / (2 * G);  // half the mean work per workgroup
+    if (c < kSplitMinSteps) c = kSplitMinSteps;
+    cs = static_cast<int>(c);
+    if (threadIdx.x == 0) {
+      // the prefix of the largest-first order that is heavy and longer than a chunk
+      int n = 0, cp = 0;
+      s_cp[0] = 0;
+      const long long tiles = static_cast<long long>(ka) * nc;
+      while (n < kMaxSplit && n < gl) {
+        const long long st = steps_at<KS>(s_lb, s_order, n);
+        if (st * G < total * per_cu || st <= c) break;
+        const int P = static_cast<int>((st + c - 1) / c);
+        if ((cp + P) * tiles > cap_tiles) break;
+        cp += P;
+        s_cp[++n] = cp;
+      }
+      s_cp[kMaxSplit + 1] = n;
+      if (blockIdx.x == 0 && header != nullptr) {
+        header[0] = n;
+        for (int i = 0; i < n; ++i) {
+          header[3 + 3 * i] = s_order[i];
+          header[4 + 3 * i] = s_cp[i + 1] - s_cp[i];
+          header[5 + 3 * i] = s_cp[i];
+        }
+      }
     }
-    const int q = static_cast<int>(i / (static_cast<long long>(kax) * ncx));
-    const int rem = static_cast<int>(i - static_cast<long long>(q) * kax * ncx);
-    const int at = (x / xc) * kax + rem / ncx;
-    const int ct = (x % xc) * ncx + rem % ncx;
+    __syncthreads();
+    ns = s_cp[kMaxSplit + 1];
+    slots = (static_cast<long long>(s_cp[ns]) + (gl - ns)) * tpg;
+    __syncthreads();
+  }
+
+  template <int BM, int BN, int KS = BK>
+  __device__ __forceinline__ bool get(long long s, const int* s_lb, const int* s_order, Tile& t,
+                                      const int* s_cp = nullptr) const {
+    const long long unit = s / tpg;
+    const int within = static_cast<int>(s - unit * tpg);
+    int x = 0, i = within;
+    if (split) {
+      x = within % kXcds;
+      i = within / kXcds;
+    }
+    const int at = (x / xc) * kax + i / ncx;
+    const int ct = (x % xc) * ncx + i % ncx;
     if (at >= ka || ct >= nc) return false;
+    int q, chunk = 0, P = 1;
+    if (ns > 0 && unit < s_cp[ns]) {
+      q = 0;
+      while (unit >= s_cp[q + 1]) ++q;
+      chunk = static_cast<int>(unit) - s_cp[q];
+      P = s_cp[q + 1] - s_cp[q];
+    } else {
+      q = ns + static_cast<int>(unit - (ns > 0 ? s_cp[ns] : 0));
+    }
     t.j = s_order[q];
     t.r_begin = s_lb[t.j];
     t.r_end = s_lb[t.j + 1];
+    t.part = -1;
+    if (P > 1) {  // chunk `chunk` of P equal step ranges
+      const int st = (t.r_end - t.r_begin + KS - 1) / KS;
+      const int per = (st + P - 1) / P;
+      const int rb = t.r_begin + chunk * per * KS;
+      t.r_end = min(t.r_end, rb + per * KS);
+      t.r_begin = rb;
+      t.part = (s_cp[q] + chunk) * ka * nc + at * nc + ct;
+    }
     t.a0 = at * BM;
     t.c0 = ct * BN;
     t.nk = (t.r_end - t.r_begin + KS - 1) / KS;
     return true;
   }
 
-  // Which slots this workgroup takes.  A tile costs its group's contraction
-  // steps.  Dealt round-robin over a largest-first list (slot s to workgroup
-  // s mod gridDim.x), every workgroup that takes one of the largest groups'
-  // tiles also takes its full share of the later ones: with Zipf-sized groups
-  // on the 32768-row backward the busiest workgroup has 450 steps against 264
-  // on average.  So tiles costing at least the mean work per workgroup (the
-  // "heavy" tiles, a prefix of the list) get a workgroup each, and the other
-  // workgroups deal the remaining slots round-robin among themselves (busiest
-  // 298 there, the cost of one heavy tile).  Workgroups keep walking the list
-  // together, so the ones running at the same time work on neighbouring
-  // tiles that share their rows in L2 (contiguous per-workgroup ranges, also
-  // tried, lose that and are 30 % slower).  NT threads; uses s_wave; ends
-  // with a barrier.
+  // Which slots this workgroup takes.  A slot costs its unit's contraction
+  // steps.  Without a row split, tiles costing at least the mean work per
+  // workgroup (the "heavy" tiles, a prefix of the list) get a workgroup each:
+  // dealt round-robin, every workgroup that takes one of the largest groups'
+  // tiles would also take its full share of the later ones (with Zipf-sized
+  // groups on the 32768-row backward the busiest workgroup had 450 steps
+  // against 264 on average).  The other slots are dealt in snake order among
+  // the remaining workgroups.  Workgroups keep walking the list together, so
+  // the ones running at the same time work on neighbouring tiles that share
+  // their rows in L2 (contiguous per-workgroup ranges, also tried, lose that
+  // and are 30 % slower).  With a row split no unit is heavy, and every slot
+  // is dealt in snake order.  NT threads; uses s_wave; ends with a barrier.
   template <int NT, int KS>
   __device__ SlotSeq dealt_slots(const int* s_lb, const int* s_order, int gl, long long* s_wave) const {
-    const long long tpg = static_cast<long long>(kax) * ncx * (split ? kXcds : 1);  // slots of one group
     const long long G = gridDim.x;
-    auto steps_of = [&](int q) {
-      const int j = s_order[q];
-      const long long st = (s_lb[j + 1] - s_lb[j] + KS - 1) / KS;
-      return st < 1 ? 1ll : st;
-    };
-    auto block_sum = [&](long long v) {
-#pragma unroll
-      for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-      __syncthreads();
-      if ((threadIdx.x & 63) == 0) s_wave[threadIdx.x >> 6] = v;
-      __syncthreads();
-      long long sum = 0;
-      for (int w = 0; w < NT / 64; ++w) sum += s_wave[w];
-      return sum;
-    };
+    const long long b = blockIdx.x;
+    if (slots <= G) return strided_slots(slots);
+    if (ns > 0) return snake_slots(0, slots, G, b);
     long long mine = 0;
-    for (int q = threadIdx.x; q < gl; q += NT) mine += tpg * steps_of(q);
-    const long long total = block_sum(mine);
+    for (int q = threadIdx.x; q < gl; q += NT) mine += tpg * steps_at<KS>(s_lb, s_order, q);
+    const long long total = block_sum<NT>(mine, s_wave);
     long long heavy = 0;
-    for (int q = threadIdx.x; q < gl; q += NT) heavy += steps_of(q) * G >= total ? 1 : 0;
-    heavy = block_sum(heavy);
-    __syncthreads();  // s_wave is reused next
+    for (int q = threadIdx.x; q < gl; q += NT) heavy += steps_at<KS>(s_lb, s_order, q) * G >= total ? 1 : 0;
+    heavy = block_sum<NT>(heavy, s_wave);
     long long H = heavy * tpg;
     if (H > G - 1) H = G - 1;
-    const long long b = blockIdx.x;
-    if (H <= 0 || slots <= G) return strided_slots(slots);
-    if (b < H) return SlotSeq{b, 1, 1};
-    const long long step = G - H;
-    return SlotSeq{b, step, b < slots ? (slots - b + step - 1) / step : 0};
+    if (H <= 0) return snake_slots(0, slots, G, b);
+    if (b < H) return SlotSeq{b, 1, 1, 0, false};
+    return snake_slots(H, slots, G - H, b - H);
   }
 };
 
@@ -1167,6 +1283,7 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
   __shared__ __attribute__((aligned(1024))) uint16_t s_tiles[S * ST];
   __shared__ int s_lb[MAXL + 1];
   __shared__ int s_aux[MAXL + 1];
+  __shared__ int s_cp[kMaxSplit + 2];
   __shared__ long long s_wave[NW];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1177,13 +1294,24 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
   if constexpr (is_trans(MODE)) {
     order_groups<NT>(s_lb, p.gl, s_aux);
     tl.init(p.gl, p.k, p.n, BM, BN);
+    if (MODE == kTransTN && p.ws != nullptr) {
+      const long long part_bytes = static_cast<long long>(BM) * BN * 4;
+      const long long cap = (p.ws_bytes - kSplitHeaderInts * 4) / part_bytes;
+      int* header = static_cast<int*>(p.ws);
+      if (blockIdx.x == 0 && threadIdx.x == 0) {
+        header[1] = BM;
+        header[2] = BN;
+      }
+      tl.template plan<NT, KSTEP>(s_lb, s_aux, p.gl, s_wave, s_cp, cap > 0 ? cap : 0, p.per_cu > 0 ? p.per_cu : 1,
+                                  header);
+    }
   } else {
     const int total_m = tile_prefix<NT>(s_lb, p.gl, BM, s_aux, s_wave);
     tl.init(total_m, p.n, TN, p.k);
   }
   auto tile_at = [&](long long s, typename Tiles::Tile& t) -> bool {
     if constexpr (is_trans(MODE))
-      return tl.template get<BM, BN, KSTEP>(s, s_lb, s_aux, t);
+      return tl.template get<BM, BN, KSTEP>(s, s_lb, s_aux, t, s_cp);
     else
       return tl.template get<BM, TN, KS>(s, s_lb, s_aux, p.gl, p.k, t);
   };
@@ -1230,12 +1358,24 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
     typename Tiles::Tile t;
     if (!tile_at(seq.at(u), t)) continue;
     char* out;
-    int r0, rlim, c0;
+    int r0, rlim, c0, clim = p.n;
+    bool of32 = p.out_f32 != 0;
+    long long ld = p.n;
     if constexpr (is_trans(MODE)) {
-      out = static_cast<char*>(p.out) + static_cast<long long>(t.j) * p.k * p.n * (p.out_f32 ? 4 : 2);
-      r0 = t.a0 + wm_off;
-      rlim = p.k;
-      c0 = t.c0 + wn_off;
+      if (t.part >= 0) {  // a row chunk of a split group: its fp32 partial tile [BM, BN]
+        out = static_cast<char*>(p.ws) + kSplitHeaderInts * 4 + static_cast<long long>(t.part) * BM * BN * 4;
+        of32 = true;
+        ld = BN;
+        r0 = wm_off;
+        rlim = min(BM, p.k - t.a0);
+        c0 = wn_off;
+        clim = min(BN, p.n - t.c0);
+      } else {
+        out = static_cast<char*>(p.out) + static_cast<long long>(t.j) * p.k * p.n * (p.out_f32 ? 4 : 2);
+        r0 = t.a0 + wm_off;
+        rlim = p.k;
+        c0 = t.c0 + wn_off;
+      }
     } else {
       out = static_cast<char*>(p.out);
       r0 = t.row0 + wm_off;
@@ -1278,8 +1418,8 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
     if constexpr (MODE == kFwdGLU)
       store_glu_tile<MI, NI, EPI_H, EPI_H, kNtStores>(acc, p.out, p.out2, p.n, r0, rlim, c0, stage);
     else
-      store_wave_tile<MI, NI, EPI, 0, NI, kNtStores, is_trans(MODE), EPI16>(acc, out, p.out_f32, p.n, r0, rlim, c0,
-                                                                            p.n, stage);
+      store_wave_tile<MI, NI, EPI, 0, NI, kNtStores, is_trans(MODE), EPI16>(acc, out, of32, ld, r0, rlim, c0, clim,
+                                                                            stage);
   }
   if constexpr (!is_trans(MODE)) zero_outside_window<NT>(p.out, p.n, p.out_f32 != 0, win);
   if constexpr (MODE == kFwdGLU)
@@ -1727,6 +1867,54 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_reduce(KArgs p, const
   }
 }
 
+// Second pass of the trans_ragged_dot row split: every element of dW[j] of
+// each split group j is the sum of its P fp32 partials, added in chunk order
+// (0, 1, ..., P - 1) and rounded once.  The plan comes from the workspace
+// header the GEMM's workgroup 0 wrote: ns, the tile shape, then (j, P, first
+// chunk) per split group.  Eight columns per thread (n % 8 == 0).
+__global__ __launch_bounds__(kThreads) void trans_split_reduce(const int* header, long long ws_bytes, void* out,
+                                                               int out_f32, int k, int n, int gl) {
+  const int ns = header[0];
+  const int BM = header[1], BN = header[2];
+  // a header the GEMM did not write in full reads as no split
+  if (ns <= 0 || ns > kMaxSplit || BM <= 0 || BN <= 0 || BM % 32 != 0 || BN % 32 != 0) return;
+  const int ka = (k + BM - 1) / BM, nc = (n + BN - 1) / BN;
+  const long long cap = (ws_bytes - kSplitHeaderInts * 4) / (static_cast<long long>(BM) * BN * 4);
+  const float* parts = reinterpret_cast<const float*>(header + kSplitHeaderInts);
+  const int cpr = n / 8;
+  const long long per_group = static_cast<long long>(k) * cpr;
+  const long long total = per_group * ns;
+  for (long long e = static_cast<long long>(blockIdx.x) * kThreads + threadIdx.x; e < total;
+       e += static_cast<long long>(gridDim.x) * kThreads) {
+    const int i = static_cast<int>(e / per_group);
+    const long long rem = e - i * per_group;
+    const int a = static_cast<int>(rem / cpr);
+    const int c = static_cast<int>(rem - static_cast<long long>(a) * cpr) * 8;
+    const int j = header[3 + 3 * i], P = header[4 + 3 * i], cp = header[5 + 3 * i];
+    const long long tiles = static_cast<long long>(ka) * nc;
+    if (j < 0 || j >= gl || P < 1 || cp < 0 || (static_cast<long long>(cp) + P) * tiles > cap) continue;
+    const long long tile = static_cast<long long>(a / BM) * nc + c / BN;
+    const long long off = static_cast<long long>(a % BM) * BN + c % BN;
+    const float* src = parts + (cp * tiles + tile) * BM * BN + off;
+    f32x4_t lo = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(src));
+    f32x4_t hi = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(src + 4));
+    for (int ch = 1; ch < P; ++ch) {
+      src += tiles * BM * BN;
+      lo += __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(src));
+      hi += __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(src + 4));
+    }
+    const long long o = (static_cast<long long>(j) * k + a) * n + c;
+    if (out_f32) {
+      store16<true>(lo, static_cast<float*>(out) + o);
+      store16<true>(hi, static_cast<float*>(out) + o + 4);
+    } else {
+      store16<true>(u32x4_t{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
+                            pack_bf16x2(hi[2], hi[3])},
+                    static_cast<uint16_t*>(out) + o);
+    }
+  }
+}
+
 KArgs make_args(const GemmProblem& p) {
   KArgs a{};
   a.a = static_cast<const uint16_t*>(p.a);
@@ -1760,6 +1948,16 @@ int grid_size(long long work_items, int per_cu) {
 enum Tile { kT64x128 = 0, kT128x128 = 1, kT128x256 = 2, kT256x256 = 3, kT128x128x2 = 4, kT64x64 = 5, kT256x256k32 = 6,
             kT128x256k32 = 7, kT128x256x2 = 8, kT128x128k32x2 = 9, kT128x128x3 = 10, kT256x128x2 = 11,
             kT128x256s3x2 = 12, kW256x256 = 13, kW128x256 = 14, kW256x256k64 = 15, kW128x512 = 16, kW128x256k32 = 17, kP256x256 = 18, kTileCount };
+
+// Output tile and workgroups per CU of each shape (as launch_tile launches them).
+struct TileShape {
+  int bm, bn, wgs;
+};
+constexpr TileShape kTileShapes[kTileCount] = {
+    {64, 128, 1},  {128, 128, 1}, {128, 256, 1}, {256, 256, 1}, {128, 128, 2}, {64, 64, 1},   {256, 256, 1},
+    {128, 256, 1}, {128, 256, 2}, {128, 128, 2}, {128, 128, 3}, {256, 128, 2}, {128, 256, 2}, {256, 256, 1},
+    {128, 256, 1}, {256, 256, 1}, {128, 512, 1}, {128, 256, 1}, {256, 256, 1}};
+TileShape tile_shape(int tile) { return kTileShapes[tile >= 0 && tile < kTileCount ? tile : kT128x128]; }
 
 // Tuning overrides set through rd_tune_set (tile sweeps only): a forced
 // forward / trans tile shape (-1: the host heuristic) and the decode path
@@ -1802,13 +2000,29 @@ int pick_trans_tile(const GemmProblem& p) {
   return p.k >= 128 && p.n >= 256 ? kT128x256s3x2 : kT128x128x2;
 }
 
+KArgs with_per_cu(KArgs a, int grid) {
+  const int cus = device_cu_count();
+  a.per_cu = (grid + cus - 1) / cus;
+  return a;
+}
+
 template <int MODE, int BM, int BN, int S, int KS = 32, int WGS = 1, int MAXL = RD_MAX_GROUPS, int WR = 2,
           int WC = 2>
 void launch_one(const KArgs& a, long long work, hipStream_t stream) {
   if constexpr (S == 0)
     grouped_gemm_regs<MODE, BM, BN><<<grid_size(work, 2), kThreads, 0, stream>>>(a);
   else
-    grouped_gemm_stream<MODE, BM, BN, S, KS, WGS, MAXL, WR, WC><<<grid_size(work, WGS), WR * WC * 64, 0, stream>>>(a);
+    grouped_gemm_stream<MODE, BM, BN, S, KS, WGS, MAXL, WR, WC><<<grid_size(work, WGS), WR * WC * 64, 0, stream>>>(
+        with_per_cu(a, grid_size(work, WGS)));
+}
+
+// launch_one for tile shape TILE, checked against kTileShapes (which sizes the trans workspace).
+template <int TILE, int MODE, int BM, int BN, int S, int KS = 32, int WGS = 1, int MAXL = RD_MAX_GROUPS, int WR = 2,
+          int WC = 2>
+void launch_checked(const KArgs& a, long long work, hipStream_t stream) {
+  static_assert(kTileShapes[TILE].bm == BM && kTileShapes[TILE].bn == BN && kTileShapes[TILE].wgs == WGS,
+                "kTileShapes must match the launched shape");
+  launch_one<MODE, BM, BN, S, KS, WGS, MAXL, WR, WC>(a, work, stream);
 }
 
 template <int MODE, int S, int KS>
@@ -1828,33 +2042,36 @@ void launch_tile(int tile, const KArgs& a, const GemmProblem& p, hipStream_t str
     // 64-deep stages (measured faster than 32-deep ones with more stages: the
     // per-stage barrier costs more than the extra depth gains); the LDS ring
     // takes 128-144 KB, 64 KB per workgroup for the two-per-CU variant
-    case kT64x128: launch_one<MODE, 64, 128, 6, 64>(a, work(64, 128), stream); break;
-    case kT128x256: launch_one<MODE, 128, 256, 3, 64>(a, work(128, 256), stream); break;
-    case kT256x256: launch_one<MODE, 256, 256, 2, 64>(a, work(256, 256), stream); break;
-    case kT128x128x2: launch_one<MODE, 128, 128, 2, 64, 2>(a, work(128, 128), stream); break;
-    case kT64x64: launch_one<MODE, 64, 64, 8, 64>(a, work(64, 64), stream); break;
-    case kT256x256k32: launch_one<MODE, 256, 256, 4, 32>(a, work(256, 256), stream); break;
-    case kT128x256k32: launch_one<MODE, 128, 256, 6, 32>(a, work(128, 256), stream); break;
-    case kT128x256x2: launch_one<MODE, 128, 256, 2, 32, 2>(a, work(128, 256), stream); break;
-    case kT128x128k32x2: launch_one<MODE, 128, 128, 3, 32, 2>(a, work(128, 128), stream); break;
-    case kT128x128x3: launch_one<MODE, 128, 128, 2, 32, 3>(a, work(128, 128), stream); break;
-    case kT256x128x2: launch_one<MODE, 256, 128, 2, 32, 2>(a, work(256, 128), stream); break;
+    case kT64x128: launch_checked<kT64x128, MODE, 64, 128, 6, 64>(a, work(64, 128), stream); break;
+    case kT128x256: launch_checked<kT128x256, MODE, 128, 256, 3, 64>(a, work(128, 256), stream); break;
+    case kT256x256: launch_checked<kT256x256, MODE, 256, 256, 2, 64>(a, work(256, 256), stream); break;
+    case kT128x128x2: launch_checked<kT128x128x2, MODE, 128, 128, 2, 64, 2>(a, work(128, 128), stream); break;
+    case kT64x64: launch_checked<kT64x64, MODE, 64, 64, 8, 64>(a, work(64, 64), stream); break;
+    case kT256x256k32: launch_checked<kT256x256k32, MODE, 256, 256, 4, 32>(a, work(256, 256), stream); break;
+    case kT128x256k32: launch_checked<kT128x256k32, MODE, 128, 256, 6, 32>(a, work(128, 256), stream); break;
+    case kT128x256x2: launch_checked<kT128x256x2, MODE, 128, 256, 2, 32, 2>(a, work(128, 256), stream); break;
+    case kT128x128k32x2: launch_checked<kT128x128k32x2, MODE, 128, 128, 3, 32, 2>(a, work(128, 128), stream); break;
+    case kT128x128x3: launch_checked<kT128x128x3, MODE, 128, 128, 2, 32, 3>(a, work(128, 128), stream); break;
+    case kT256x128x2: launch_checked<kT256x128x2, MODE, 256, 128, 2, 32, 2>(a, work(256, 128), stream); break;
     case kT128x256s3x2:  // a 3-slot ring for two workgroups per CU fits only with num_local <= 512
       if (p.num_local <= 512)
-        launch_one<MODE, 128, 256, 3, 32, 2, 512>(a, work(128, 256), stream);
+        launch_checked<kT128x256s3x2, MODE, 128, 256, 3, 32, 2, 512>(a, work(128, 256), stream);
       else
-        launch_one<MODE, 128, 256, 2, 32, 2>(a, work(128, 256), stream);
+        launch_checked<kT128x256s3x2, MODE, 128, 256, 2, 32, 2>(a, work(128, 256), stream);
       break;
     // eight waves (two per SIMD) sharing one ring: 4 x 2 waves of 64 x 128,
     // 2 x 4 waves of 64 x 64, and the 256 x 256 tile with 64-deep stages
-    case kW256x256: launch_one<MODE, 256, 256, 4, 32, 1, RD_MAX_GROUPS, 4, 2>(a, work(256, 256), stream); break;
-    case kW128x256: launch_one<MODE, 128, 256, 3, 64, 1, RD_MAX_GROUPS, 2, 4>(a, work(128, 256), stream); break;
-    case kW256x256k64: launch_one<MODE, 256, 256, 2, 64, 1, RD_MAX_GROUPS, 4, 2>(a, work(256, 256), stream); break;
-    case kW128x512: launch_one<MODE, 128, 512, 3, 32, 1, RD_MAX_GROUPS, 2, 4>(a, work(128, 512), stream); break;
-    case kW128x256k32: launch_one<MODE, 128, 256, 6, 32, 1, RD_MAX_GROUPS, 2, 4>(a, work(128, 256), stream); break;
+    case kW256x256: launch_checked<kW256x256, MODE, 256, 256, 4, 32, 1, RD_MAX_GROUPS, 4, 2>(a, work(256, 256), stream); break;
+    case kW128x256: launch_checked<kW128x256, MODE, 128, 256, 3, 64, 1, RD_MAX_GROUPS, 2, 4>(a, work(128, 256), stream); break;
+    case kW256x256k64: launch_checked<kW256x256k64, MODE, 256, 256, 2, 64, 1, RD_MAX_GROUPS, 4, 2>(a, work(256, 256), stream); break;
+    case kW128x512: launch_checked<kW128x512, MODE, 128, 512, 3, 32, 1, RD_MAX_GROUPS, 2, 4>(a, work(128, 512), stream); break;
+    case kW128x256k32: launch_checked<kW128x256k32, MODE, 128, 256, 6, 32, 1, RD_MAX_GROUPS, 2, 4>(a, work(128, 256), stream); break;
     // eight waves in two ping-pong groups on 256 x 256 tiles, a 2-slot ring of 64-deep stages
-    case kP256x256: launch_pp<MODE, 2, 64>(a, work(256, 256), stream); break;
-    default: launch_one<MODE, 128, 128, 4, 64>(a, work(128, 128), stream); break;
+    case kP256x256:
+      static_assert(kTileShapes[kP256x256].bm == 256 && kTileShapes[kP256x256].bn == 256, "pp tile shape");
+      launch_pp<MODE, 2, 64>(a, work(256, 256), stream);
+      break;
+    default: launch_checked<kT128x128, MODE, 128, 128, 4, 64>(a, work(128, 128), stream); break;
   }
 }
 
@@ -2053,10 +2270,34 @@ int launch_trans_fp8(const GemmProblem& p, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? RD_OK : RD_EHIP;
 }
 
-int launch_trans(const GemmProblem& p, hipStream_t stream) {
-  const KArgs a = make_args(p);
+size_t trans_workspace_size(const GemmProblem& p) {
+  if (!fits_32bit(p.m, p.k) || !fits_32bit(p.m, p.n)) return 0;  // the fallback pipeline does not split
+  const int tile = pick_trans_tile(p);
+  if (tile == kP256x256) return 0;
+  const TileShape ts = tile_shape(tile);
+  const long long tiles = static_cast<long long>(p.num_local) * ((p.k + ts.bm - 1) / ts.bm) *
+                          ((p.n + ts.bn - 1) / ts.bn);
+  const long long G = grid_size(tiles, ts.wgs);
+  // split groups carry at least the mean work per CU (no less than the mean
+  // per workgroup) and chunks at least half the mean per workgroup, so the
+  // partials never exceed 3 G tiles
+  return kSplitHeaderInts * 4 + static_cast<size_t>(3 * G) * ts.bm * ts.bn * 4;
+}
+
+int launch_trans(const GemmProblem& p, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  KArgs a = make_args(p);
   if (fits_32bit(p.m, p.k) && fits_32bit(p.m, p.n)) {
-    launch_tile<kTransTN>(pick_trans_tile(p), a, p, stream);
+    const int tile = pick_trans_tile(p);
+    const bool split = workspace != nullptr && workspace_bytes > kSplitHeaderInts * 4 && tile != kP256x256;
+    if (split) {
+      a.ws = workspace;
+      a.ws_bytes = static_cast<long long>(workspace_bytes);
+    }
+    launch_tile<kTransTN>(tile, a, p, stream);
+    if (split)
+      trans_split_reduce<<<grid_size(static_cast<long long>(p.k) * (p.n / 8) / kThreads + 1, 4), kThreads, 0,
+                           stream>>>(static_cast<const int*>(workspace), static_cast<long long>(workspace_bytes), p.out,
+                                     p.out_f32 ? 1 : 0, p.k, p.n, p.num_local);
   } else {
     const long long tiles = static_cast<long long>(p.num_local) * ((p.k + 127) / 128) * ((p.n + 127) / 128);
     launch_one<kTransTN, 128, 128, 0>(a, tiles, stream);

@@ -35,7 +35,11 @@ DecodePlan plan_decode(const GemmProblem& p, bool trans_rhs);
 // workspace may be null; the decode path runs only with ws_bytes of it.
 int launch_forward(const GemmProblem& p, bool trans_rhs, void* workspace, size_t workspace_bytes,
                    hipStream_t stream);
-int launch_trans(const GemmProblem& p, hipStream_t stream);
+// trans_ragged_dot; with a workspace, groups long enough to hold up the grid
+// are split over rows (fp32 partials, then a fixed-order reduction kernel).
+int launch_trans(const GemmProblem& p, void* workspace, size_t workspace_bytes, hipStream_t stream);
+// Workspace bytes that let launch_trans split every group that qualifies (0: it never splits).
+size_t trans_workspace_size(const GemmProblem& p);
 // launch_forward (plain form) with the decode path's partial sums in the library's static device
 // scratch (RD_NOALLOC_SCRATCH_BYTES); RD_ESCRATCH when the sizes need more.
 int launch_forward_noalloc(const GemmProblem& p, hipStream_t stream);

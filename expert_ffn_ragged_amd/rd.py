@@ -19,7 +19,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librd.so")
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 RD_OK, RD_EINVAL, RD_EUNSUPPORTED, RD_EHIP, RD_ESCRATCH = 0, 1, 2, 3, 4
 RD_NOALLOC_SCRATCH_BYTES = 80 << 20
 RD_BF16, RD_F32 = 0, 1
@@ -343,8 +343,13 @@ def ragged_dot_glu(x, wi, group_sizes, group_offset=None, limit=None, act=None, 
 
 
 def trans_ragged_dot(x, dy, group_sizes, num_local=None, group_offset=None, limit=None,
-                     out_dtype=torch.float32, out=None, workspace=None, stream=None):
-    """dw[j] = x_j^T @ dy_j over the rows of local group j; [num_local, k, n]."""
+                     out_dtype=torch.float32, out=None, workspace=None, row_split=True, stream=None):
+    """dw[j] = x_j^T @ dy_j over the rows of local group j; [num_local, k, n].
+
+    ``workspace``: optional uint8 GPU scratch for the row split of long groups, used as given (a
+    smaller one than ``rd_trans_workspace_size`` splits fewer groups); without it one of that size is
+    allocated.  ``row_split=False`` passes no workspace (no group is split).
+    """
     _need(x, "x", torch.bfloat16, 2)
     _need(dy, "dy", torch.bfloat16, 2)
     _need(group_sizes, "group_sizes", torch.int32, 1)
@@ -362,16 +367,26 @@ def trans_ragged_dot(x, dy, group_sizes, num_local=None, group_offset=None, limi
     if tuple(out.shape) != (gl, k, n) or out.dtype not in _DTYPES:
         raise ValueError("out must be [num_local, k, n] bf16 or float32")
     lib = library()
-    ws_bytes = lib.rd_trans_workspace_size(m, k, n, gl)
-    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
-        _on_stream(stream, workspace)
+    ws_bytes = 0
+    if row_split and workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1)
+        ws_bytes = workspace.numel()
+    elif row_split:
+        ws_bytes = lib.rd_trans_workspace_size(m, k, n, gl)
+        if ws_bytes:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+            _on_stream(stream, workspace)
     if fresh:
         _on_stream(stream, out)
     _check(lib.rd_trans(_ptr(x), _ptr(dy), _ptr(group_sizes), group_sizes.numel(), _ptr(group_offset), gl,
                         _ptr(limit), _ptr(out), _DTYPES[out.dtype], m, k, n,
                         _ptr(workspace) if ws_bytes else None, ws_bytes, _stream(stream)))
     return out
+
+
+def trans_workspace_size(m, k, n, num_local):
+    """Bytes of workspace that let trans_ragged_dot split every group that qualifies (0: none can)."""
+    return int(library().rd_trans_workspace_size(m, k, n, num_local))
 
 
 def glu_fwd(fused, limit=None, out=None, stream=None):

@@ -78,6 +78,14 @@ def group_sizes(workload, seed=None, empty_at=1):
     raise ValueError(f"unknown workload {workload}")
 
 
+def hot_expert_sizes(total=32768, hot_rows=19660, hot=5, G=64, s=1.1, seed=11):
+    """Group sizes with one hot expert: ``hot_rows`` rows in group ``hot``, the rest Zipf(s) over the
+    other G - 1 groups (the backward's 32768 rows with 60 % in one expert, by default)."""
+    rng = np.random.default_rng(seed)
+    rest = multinomial_sizes(total - hot_rows, zipf_probs(G - 1, s, rng), rng)
+    return np.concatenate([rest[:hot], [hot_rows], rest[hot:]]).astype(np.int32)
+
+
 def random_sizes(G, total, seed, empty=()):
     """Uniform multinomial sizes with the listed groups forced empty (for sweeps)."""
     rng = np.random.default_rng(seed)

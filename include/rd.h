@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define RD_ABI_VERSION 6
+#define RD_ABI_VERSION 7
 
 /* status codes */
 #define RD_OK 0
@@ -197,8 +197,24 @@ int rd_forward_fp8(const void* x, const void* w, const int32_t* group_sizes, int
  *
  * With m == 0, x and dy may be NULL and every dw[j] is written as +0.
  *
- * workspace/workspace_bytes: caller-owned device scratch of at least
- * rd_trans_workspace_size(...) bytes (may be NULL when that size is 0).
+ * Row split: with a workspace, a group whose rows cost at least the mean
+ * work per CU (and more than one chunk) is cut into row chunks of equal
+ * length, decided on the device from group_sizes.  Each chunk's tile
+ * goes to the workspace as an fp32 partial, and a second kernel adds a
+ * tile's partials in chunk order and rounds once (per-block partials summed
+ * after the pass, never a read-modify-write shared by workgroups: the race
+ * lesson of [MaxText]'s unsort review).  Results are deterministic: the same
+ * inputs, sizes and workspace_bytes give the same bits; a different
+ * workspace_bytes may change which groups are split, and with it the
+ * float32 summation order (within rounding).  The bf16 result is the RNE
+ * rounding of the f32 result of the same call shape.
+ *
+ * workspace/workspace_bytes: NULL/0 (no split), or caller-owned device
+ * scratch, 16-byte aligned; rd_trans_workspace_size(m, k, n, num_local)
+ * bytes let every qualifying group split (0 when the sizes never split:
+ * m == 0, or operands past 4 GiB), a smaller size splits fewer groups.  The
+ * workspace must not be in use by another call on another stream.
+ * RD_EINVAL for workspace_bytes > 0 with a NULL or misaligned workspace.
  */
 size_t rd_trans_workspace_size(int64_t m, int64_t k, int64_t n, int32_t num_local);
 int rd_trans(const void* x, const void* dy, const int32_t* group_sizes, int32_t num_groups,

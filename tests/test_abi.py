@@ -46,10 +46,40 @@ def test_links_the_same_hip_runtime_soname_as_torch():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.rd_abi_version() == rd.ABI_VERSION == 6
+    assert lib.rd_abi_version() == rd.ABI_VERSION == 7
     for s in (0, 1, 2, 3, 99):
         assert isinstance(lib.rd_status_string(s), bytes)
-    assert lib.rd_trans_workspace_size(100, 64, 64, 4) == 0
+
+
+def test_trans_workspace_size(lib):
+    """The row-split workspace: a header plus fp32 partial tiles; none when nothing can split."""
+    size = lib.rd_trans_workspace_size
+    assert size(0, 1024, 4096, 64) == 0                 # no rows
+    assert size(1 << 21, 1024, 4096, 64) == 0           # x past 4 GiB: the fallback pipeline never splits
+    assert size(100, 12, 64, 4) == 0                    # k not a multiple of 8: rejected sizes
+    for m, k, n, gl in ((100, 64, 64, 4), (32768, 1024, 4096, 64), (8192, 4096, 2048, 64)):
+        b = size(m, k, n, gl)
+        assert b > 256 and (b - 256) % (128 * 128 * 4) == 0, (m, k, n, gl, b)
+    # bounded by three partial tiles per workgroup of the grid (at most three workgroups per CU)
+    assert size(32768, 1024, 4096, 64) <= 256 + 3 * 3 * 256 * 256 * 256 * 4
+
+
+def _trans(lib, **kw):
+    a = dict(x=16, dy=16, gs=16, G=4, off=None, gl=4, limit=None, dw=16, dt=0, m=8, k=8, n=8, ws=None, ws_bytes=0)
+    a.update(kw)
+    v = lambda p: None if p is None else ctypes.c_void_p(p)
+    return lib.rd_trans(v(a["x"]), v(a["dy"]), v(a["gs"]), a["G"], v(a["off"]), a["gl"], v(a["limit"]), v(a["dw"]),
+                        a["dt"], a["m"], a["k"], a["n"], v(a["ws"]), a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=None, ws_bytes=4096), rd.RD_EINVAL),   # a workspace size without a workspace
+    (dict(ws=24, ws_bytes=4096), rd.RD_EINVAL),     # misaligned workspace
+    (dict(dt=7), rd.RD_EINVAL),
+    (dict(k=12), rd.RD_EUNSUPPORTED),
+])
+def test_trans_rejects_before_launch(lib, kw, status):
+    assert _trans(lib, **kw) == status
 
 
 def _fwd(lib, **kw):
