@@ -14,6 +14,8 @@ resident in HBM.  Each step is bracketed by HIP events on the stream the
 kernels run on, with one more event between dx and dW, which gives each
 kernel's time; the slower kernel is reported against its roofline.  The
 same step is also timed warm (steps back to back, events only at the ends).
+Before the first timed loop the step runs untimed, cold, SETTLE_STEPS
+times, so the timed loops see the steady state of repeated steps.
 The other workloads (up-projection forward+backward, decode, window+limit,
 GLU and unsort over the packed buffer, fp8) are reported under ``extra``.
 Inputs are synthetic and seeded (expert_ffn_ragged_amd/workloads.py).
@@ -49,6 +51,9 @@ def parse():
                     help="time every tile shape of every grouped GEMM on the workloads and print the table")
     ap.add_argument("--profile", choices=("backward", "upproj", "decode", "packed"),
                     help="only run one workload's kernels, --warmup + --steps times each, for a profiler")
+    ap.add_argument("--settle", type=int, default=0,
+                    help="with --profile: untimed passes before the warmup, flushed with --cold (the headline "
+                         f"settles for {SETTLE_STEPS} cold steps)")
     ap.add_argument("--cold", action="store_true",
                     help="with --profile: flush L2 and the MALL (a 512 MiB write) before every pass")
     ap.add_argument("--copy-calib", action="store_true",
@@ -108,6 +113,27 @@ def timed_ops(ops, steps, warmup):
     if COLD["on"]:  # the flushes sit between the events: the step is the sum of its ops
         gpu_ms = sum(per_op.values()) * steps
     return wall, gpu_ms, per_op
+
+
+SETTLE_STEPS = 300  # untimed cold steps before the first timed loop of a process (about 0.25 s)
+
+
+def settle(ops, steps=SETTLE_STEPS, cold=True):
+    """Run the ops untimed `steps` times, each after a cache flush when cold (synchronizing every 50),
+    so the timed loops see the steady state of repeated steps.  Measured on the backward: the first
+    cold loop of a process (5 warm-up + 20 timed steps) took 0.80 ms a step, every later one 0.70-0.72;
+    1500 warm steps before it, or 300 flushes alone, left it at 0.77; 300 cold steps removed it."""
+    import torch
+
+    for i in range(steps):
+        if cold:
+            flush_caches()
+        for _, fn in ops:
+            fn()
+        if i % 50 == 49:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return steps
 
 
 def step_timed(ops, steps, warmup):
@@ -206,6 +232,7 @@ def backward(steps, warmup):
         ("ragged_dot_trans_rhs", lambda: rd.ragged_dot(dy, w, gs, trans_rhs=True, out=dx)),
         ("trans_ragged_dot", lambda: rd.trans_ragged_dot(x, dy, gs, out=dw)),
     ]
+    settled = settle(ops)
     COLD["on"] = True
     wall, cold_ms, cold_per = timed_ops(ops, steps, warmup)
     cold_pct = {name: PERCENTILES[name] for name, _ in ops}
@@ -218,7 +245,8 @@ def backward(steps, warmup):
     # written once (dW of an empty expert is written as zeros)
     nbytes = {"ragged_dot_trans_rhs": rows * n * b + nonempty * k * n * b + rows * k * b,
               "trans_ragged_dot": rows * k * b + rows * n * b + d["G"] * k * n * b}
-    return dict(rows=rows, m=m, k=k, n=n, G=d["G"], wall=wall, cold_ms=cold_ms / steps, cold_per=cold_per,
+    return dict(rows=rows, m=m, k=k, n=n, G=d["G"], wall=wall, settle_steps=settled, cold_ms=cold_ms / steps,
+                cold_per=cold_per,
                 cold_pct=cold_pct, warm_per=warm_per, warm_step=warm_step, bytes=nbytes,
                 flops={"ragged_dot_trans_rhs": flop, "trans_ragged_dot": flop}, step_flop=2 * flop,
                 tensors=(x, w, dy, d["gs_host"]))
@@ -637,9 +665,10 @@ def sweep(steps):
     torch.cuda.empty_cache()
 
 
-def profile_run(which, steps, warmup, cold=False):
+def profile_run(which, steps, warmup, cold=False, settle_steps=0):
     """One workload's kernels and nothing else (no timing, no oracle), for rocprofv3 runs; with cold, the
-    caches are flushed before every pass as in the headline's timing."""
+    caches are flushed before every pass as in the headline's timing; settle_steps untimed passes (no
+    flushes) come first, as before the headline's timed loops."""
     import torch
 
     from expert_ffn_ragged_amd import rd, workloads
@@ -680,13 +709,16 @@ def profile_run(which, steps, warmup, cold=False):
         dot = torch.empty((d["m"],), dtype=torch.float32, device="cuda")
         ops = [lambda: rd.glu_fwd(d["fused"], lim, out=g), lambda: rd.glu_bwd(d["fused"], d["d_out"], lim, out=gb),
                lambda: rd.unsort_bwd_rows(d["ug"], d["uy"], d["uw"], lim, grad=grad, dot=dot)]
+    if settle_steps:
+        settle([(None, fn) for fn in ops], settle_steps, cold)
     for _ in range(warmup + steps):
         if cold:
             flush_caches()
         for fn in ops:
             fn()
     torch.cuda.synchronize()
-    print(json.dumps({"profile": which, "launches_per_op": warmup + steps, "cold": cold}), flush=True)
+    print(json.dumps({"profile": which, "launches_per_op": settle_steps + warmup + steps, "settle": settle_steps,
+                      "cold": cold}), flush=True)
 
 
 def main():
@@ -718,7 +750,7 @@ def main():
                 b.copy_(a)
             torch.cuda.synchronize()
             del a, b
-        profile_run(args.profile, args.steps, args.warmup, args.cold)
+        profile_run(args.profile, args.steps, args.warmup, args.cold, args.settle)
         return
     if args.copy_calib:
         a = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
@@ -753,7 +785,9 @@ def main():
                                   p10_p50_p90_ms=r["cold_pct"][name])
                        for name, ms in r["cold_per"].items()},
         "timing": ("cold: L2 and MALL flushed (512 MiB write) before each step, outside the events; HIP events "
-                   "before dx, between dx and dW and after dW on the stream both run on"),
+                   "before dx, between dx and dW and after dW on the stream both run on; first "
+                   f"{r['settle_steps']} untimed cold steps to reach the steady state of repeated steps, then "
+                   "the warmup steps"),
         "warm": {"ms_per_step": round(r["warm_step"], 4),
                  "TFLOP/s": round(r["step_flop"] / r["warm_step"] / 1e9, 1),
                  "per_kernel_ms": {name: round(ms, 4) for name, ms in r["warm_per"].items()},
