@@ -512,6 +512,7 @@ def api_region(iters=5):
     dfused = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
     dx = torch.empty((m, k), dtype=torch.bfloat16, device="cuda")
     dw = torch.empty((w.shape[0], k, n), dtype=torch.bfloat16, device="cuda")
+    wst = torch.empty(max(rd.trans_workspace_size(m, k, n, w.shape[0]), 16), dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
     torch.cuda.mem_get_info()  # region start mark
     for i in range(iters):
@@ -522,7 +523,7 @@ def api_region(iters=5):
         rd.glu_fwd(fused, out=act)
         rd.glu_bwd(fused, d_act, out=dfused)
         rd.ragged_dot(dfused, w, gs, trans_rhs=True, out=dx)
-        rd.trans_ragged_dot(x, dfused, gs, out=dw)
+        rd.trans_ragged_dot(x, dfused, gs, out=dw, workspace=wst)
     torch.cuda.mem_get_info()  # region end mark
     torch.cuda.synchronize()
     print(json.dumps({"api_region": "done", "iters": iters}), flush=True)

@@ -1871,8 +1871,10 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_reduce(KArgs p, const
 // each split group j is the sum of its P fp32 partials, added in chunk order
 // (0, 1, ..., P - 1) and rounded once.  The plan comes from the workspace
 // header the GEMM's workgroup 0 wrote: ns, the tile shape, then (j, P, first
-// chunk) per split group.  Eight columns per thread (n % 8 == 0).
-__global__ __launch_bounds__(kThreads) void trans_split_reduce(const int* header, long long ws_bytes, void* out,
+// chunk) per split group.  Eight columns per thread (n % 8 == 0).  Workgroups
+// of 1024 threads, one per CU: the launch costs little when nothing was split.
+constexpr int kReduceThreads = 1024;
+__global__ __launch_bounds__(kReduceThreads) void trans_split_reduce(const int* header, long long ws_bytes, void* out,
                                                                int out_f32, int k, int n, int gl) {
   const int ns = header[0];
   const int BM = header[1], BN = header[2];
@@ -1884,8 +1886,8 @@ __global__ __launch_bounds__(kThreads) void trans_split_reduce(const int* header
   const int cpr = n / 8;
   const long long per_group = static_cast<long long>(k) * cpr;
   const long long total = per_group * ns;
-  for (long long e = static_cast<long long>(blockIdx.x) * kThreads + threadIdx.x; e < total;
-       e += static_cast<long long>(gridDim.x) * kThreads) {
+  for (long long e = static_cast<long long>(blockIdx.x) * kReduceThreads + threadIdx.x; e < total;
+       e += static_cast<long long>(gridDim.x) * kReduceThreads) {
     const int i = static_cast<int>(e / per_group);
     const long long rem = e - i * per_group;
     const int a = static_cast<int>(rem / cpr);
@@ -2295,8 +2297,8 @@ int launch_trans(const GemmProblem& p, void* workspace, size_t workspace_bytes, 
     }
     launch_tile<kTransTN>(tile, a, p, stream);
     if (split)
-      trans_split_reduce<<<grid_size(static_cast<long long>(p.k) * (p.n / 8) / kThreads + 1, 4), kThreads, 0,
-                           stream>>>(static_cast<const int*>(workspace), static_cast<long long>(workspace_bytes), p.out,
+      trans_split_reduce<<<grid_size(static_cast<long long>(p.k) * (p.n / 8) / kReduceThreads + 1, 1),
+                           kReduceThreads, 0, stream>>>(static_cast<const int*>(workspace), static_cast<long long>(workspace_bytes), p.out,
                                      p.out_f32 ? 1 : 0, p.k, p.n, p.num_local);
   } else {
     const long long tiles = static_cast<long long>(p.num_local) * ((p.k + 127) / 128) * ((p.n + 127) / 128);

@@ -46,6 +46,7 @@ OP_OF_KERNEL = (
     (r"glu_bwd_kernel", "glu_bwd"),
     (r"decode_streamk_gemm", "decode_gemm"),
     (r"decode_streamk_reduce", "decode_reduce"),
+    (r"trans_split_reduce", "trans_split_reduce"),
 )
 
 
@@ -174,8 +175,8 @@ def stats_summary(stats_dir, command, title, skip=0):
              "with `TMPDIR=/tmp` exported):", "", "```", command, "```", "",
              f"source digest: {source_digest()}", ""]
     if skip:
-        lines += [f"The last two columns leave out each kernel's first {skip} dispatches (the command's warm-up "
-                  "launches), from the kernel trace of the same run.", ""]
+        lines += [f"The last two columns leave out each kernel's first {skip} dispatches (the command's untimed "
+                  "settle and warm-up launches), from the kernel trace of the same run.", ""]
     lines += ["| kernel | calls | average (us) | min (us) | max (us) |" + (" timed calls | timed average (us) |"
                                                                           if skip else ""),
               "|---|---|---|---|---|" + ("---|---|" if skip else "")]
