@@ -74,6 +74,8 @@ def test_moe_mlp_training_step_graph_replays_follow_device_group_sizes():
         out = ag.moe_mlp(x, wi, wo, gs)
         return (out,) + torch.autograd.grad(out, (x, wi, wo), dout)
 
+    # warm up and capture on the same side stream, so the leaves' gradient accumulators (created by
+    # the warm-up) belong to the stream the captured backward runs on
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -83,7 +85,7 @@ def test_moe_mlp_training_step_graph_replays_follow_device_group_sizes():
     torch.cuda.synchronize()
 
     graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
+    with torch.cuda.graph(graph, stream=side):
         captured = train_step()
 
     sizes = [workloads.random_sizes(G, m, seed=s, empty=e) for s, e in ((80, ()), (81, (0, 5)), (82, (15,)))]
@@ -93,7 +95,8 @@ def test_moe_mlp_training_step_graph_replays_follow_device_group_sizes():
         graph.replay()
         torch.cuda.synchronize()
         got = [t.clone() for t in captured]
-        want = train_step()
+        with torch.cuda.stream(side):  # the eager reference on the stream the accumulators belong to
+            want = train_step()
         torch.cuda.synchronize()
         for name, a, b in zip(("out", "dx", "dwi", "dwo"), got, want):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"replay {i}: {name} differs from eager"
