@@ -241,7 +241,13 @@ __device__ __forceinline__ u32x4_t make_rsrc(const void* base, unsigned long lon
 // pipeline below waits for these loads explicitly with s_waitcnt vmcnt.
 // M0 holds the LDS base and needs one wait state before the load uses it;
 // it is declared clobbered, so the compiler re-establishes any M0 value of
-// its own after the load.
+// its own after the load.  The write of M0 stays inside the statement: with
+// M0 as an input operand instead, the compiler wrote the next load's M0
+// right after this load, and trans_ragged_dot results were wrong from call
+// to call.  (clang notes that a reserved register in a clobber list may not
+// be preserved; here that is the intent, so the note is silenced.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(u32x4_t r, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
@@ -257,6 +263,7 @@ __device__ __forceinline__ void dma16_nt(u32x4_t r, uint32_t lds_addr, uint32_t 
                : "s"(lds_addr), "v"(voff), "s"(r), "s"(soff)
                : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // Scalar operands of dma16 are wave-uniform by construction; readfirstlane
 // states it, so the compiler keeps them in SGPRs as the instruction needs.
