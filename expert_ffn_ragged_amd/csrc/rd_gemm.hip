@@ -241,15 +241,18 @@ __device__ __forceinline__ u32x4_t make_rsrc(const void* base, unsigned long lon
 // pipeline below waits for these loads explicitly with s_waitcnt vmcnt.
 // M0 holds the LDS base and needs one wait state before the load uses it;
 // it is declared clobbered, so the compiler re-establishes any M0 value of
-// its own after the load.  The write of M0 stays inside the statement: with
-// M0 as an input operand instead, the compiler wrote the next load's M0
-// right after this load, and trans_ragged_dot results were wrong from call
-// to call.  (clang notes that a reserved register in a clobber list may not
-// be preserved; here that is the intent, so the note is silenced.)
+// its own after the load.  M0 must also not change in the cycle right after
+// the load: a build where the compiler wrote the next load's M0 immediately
+// after it (M0 as an input operand of the statement) gave wrong
+// trans_ragged_dot results from call to call, and every working build had at
+// least one instruction in between.  So the statement writes M0 itself and
+// ends with a wait state of its own.  (clang notes that a reserved register
+// in a clobber list may not be preserved; here that is the intent, so the
+// note is silenced.)
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(u32x4_t r, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds\n\ts_nop 0"
                :
                : "s"(lds_addr), "v"(voff), "s"(r), "s"(soff)
                : "memory", "m0");
@@ -258,7 +261,7 @@ __device__ __forceinline__ void dma16(u32x4_t r, uint32_t lds_addr, uint32_t vof
 // The same load marked non-temporal, for data read exactly once (the decode
 // path's weight stream): it does not displace reused lines from the caches.
 __device__ __forceinline__ void dma16_nt(u32x4_t r, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds\n\ts_nop 0"
                :
                : "s"(lds_addr), "v"(voff), "s"(r), "s"(soff)
                : "memory", "m0");
