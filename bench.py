@@ -726,8 +726,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the ragged-dot path runs on a single MI355X here; "
-              "multi-GPU (expert-parallel) runs are not part of this build", file=sys.stderr)
+        print("bench.py measures one GPU: the ragged-dot kernels run on one MI355X's share of the work; "
+              "multi-GPU (expert-parallel) runs are not supported by this benchmark", file=sys.stderr)
         sys.exit(2)
     import torch
 

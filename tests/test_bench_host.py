@@ -1,6 +1,6 @@
 """Host logic of bench.py, without a GPU: the roofline a kernel is reported
 against (HBM below the ridge point, MFMA at or above it) and the refusal of
-multi-GPU runs, which this one-GPU build does not measure."""
+multi-GPU runs, which the one-GPU benchmark does not measure."""
 
 import os
 import subprocess
