@@ -40,7 +40,7 @@ METRIC = "ragged_dot TFLOP/s (valid rows) + % bf16 MFMA peak; decode-shape HBM G
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--all", action="store_true",
@@ -303,9 +303,62 @@ def extra_workloads(steps, warmup):
         "ms": round(per["decode"], 4), "GB/s": round(nb / per["decode"] / 1e6, 1),
         "hbm_frac": round(nb / per["decode"] / 1e6 / HBM_PEAK_GBS, 4), "algorithmic_bytes": int(nb),
         "traffic": None if t is None else int(t), "p10_p50_p90_ms": PERCENTILES.get("decode")}
+    out["decode_layer_graph_m512"] = decode_graph(d, ws, steps, warmup)
     del d, o
     torch.cuda.empty_cache()
     return out
+
+
+def decode_graph(d, ws, steps, warmup):
+    """The decode layer (ragged_dot then GLU, one device-resident group_sizes) captured as one graph and
+    replayed; between replays a device-side copy rewrites group_sizes (alternating two size vectors),
+    outside the events.  After the timed replays, the last replay's output is checked bit for bit
+    against the same layer run eagerly on the same sizes."""
+    import torch
+
+    from expert_ffn_ragged_amd import rd
+
+    m, n = d["m"], d["n"]
+    gs_a, gs_b = d["gs"].clone(), torch.roll(d["gs"], 1).contiguous()
+    gs = gs_a.clone()
+    o = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    act = torch.empty((m, n // 2), dtype=torch.bfloat16, device="cuda")
+
+    def layer():
+        rd.ragged_dot(d["x"], d["w"], gs, out=o, workspace=ws)
+        rd.glu_fwd(o, out=act)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        layer()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(warmup + steps):
+        gs.copy_(gs_b if i % 2 else gs_a)  # device-side rewrite, outside the events
+        if i >= warmup:
+            evs[i - warmup][0].record(stream)
+        graph.replay()
+        if i >= warmup:
+            evs[i - warmup][1].record(stream)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in evs)
+    got = act.clone()
+    last = gs_b if (warmup + steps - 1) % 2 else gs_a
+    gs.copy_(last)
+    layer()
+    torch.cuda.synchronize()
+    if not torch.equal(got.view(torch.int16), act.view(torch.int16)):
+        raise RuntimeError("decode graph replay differs from the eager layer")
+    q = lambda f: t[min(len(t) - 1, int(round(f * (len(t) - 1))))]
+    return {"ms": round(sum(t) / len(t), 4), "p10_p50_p90_ms": [round(q(0.1), 4), round(q(0.5), 4), round(q(0.9), 4)],
+            "timing": "replays of one captured graph (ragged_dot -> GLU), group_sizes rewritten on the device "
+                      "between replays (outside the events); last replay checked bitwise against eager"}
 
 
 def extra_all(steps):
@@ -583,11 +636,21 @@ def cpu_baseline(x, w, dy, gs_host, budget_s=15.0):
             break
     flop = 2 * 2.0 * rows * k * n
     nz = int((gs_host > 0).sum())
+    # the elementwise GLU oracle (single-threaded NumPy, its exp written out step by step) on 4096 rows of a
+    # [gate | up] buffer, h = 1024
+    from expert_ffn_ragged_amd.workloads import bf16_normal
+
+    fused = bits(bf16_normal((4096, 2048), 1.0, 4004, "cpu"))
+    t0 = time.perf_counter()
+    oracle.glu_fwd(fused)
+    glu_s = time.perf_counter() - t0
     return {"value": round(flop / spent / 1e12, 6), "unit": "TFLOP/s", "cores": blas, "kind": "oracle",
             "sample": f"oracle trans_rhs ragged_dot (dx) + trans_ragged_dot (dW), float64, on the timed backward "
                       f"tensors, {experts} of {nz} non-empty experts largest first ({rows} of {int(gs_host.sum())} "
                       f"rows), {spent:.1f} s",
-            "cpu_model": model, "affinity_cores": affinity, "blas_threads": blas}
+            "cpu_model": model, "affinity_cores": affinity, "blas_threads": blas,
+            "glu_fwd": {"value": round(4096 * 6 * 1024 / glu_s / 1e9, 4), "unit": "GB/s", "cores": 1,
+                        "sample": f"oracle glu_fwd on 4096 rows, h 1024 (float32 NumPy), {glu_s:.3f} s"}}
 
 
 def sweep(steps):
