@@ -310,23 +310,29 @@ def extra_workloads(steps, warmup):
 
 
 def decode_graph(d, ws, steps, warmup):
-    """The decode layer (ragged_dot then GLU, one device-resident group_sizes) captured as one graph and
-    replayed; between replays a device-side copy rewrites group_sizes (alternating two size vectors),
-    outside the events.  After the timed replays, the last replay's output is checked bit for bit
-    against the same layer run eagerly on the same sizes."""
+    """The decode layer (wi ragged_dot, GLU, wo ragged_dot, one device-resident group_sizes; wo is
+    [128, 768, 4096]) captured as one graph and replayed; between replays a device-side copy rewrites
+    group_sizes (alternating two size vectors), outside the events.  After the timed replays, the last
+    replay's output is checked bit for bit against the same layer run eagerly on the same sizes."""
     import torch
 
-    from expert_ffn_ragged_amd import rd
+    from expert_ffn_ragged_amd import rd, workloads
 
     m, n = d["m"], d["n"]
+    h, d_out = n // 2, 4096
     gs_a, gs_b = d["gs"].clone(), torch.roll(d["gs"], 1).contiguous()
     gs = gs_a.clone()
     o = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
-    act = torch.empty((m, n // 2), dtype=torch.bfloat16, device="cuda")
+    act = torch.empty((m, h), dtype=torch.bfloat16, device="cuda")
+    wo = workloads.bf16_normal((d["G"], h, d_out), 0.02, 2009, "cuda")
+    out = torch.empty((m, d_out), dtype=torch.bfloat16, device="cuda")
+    ws2 = torch.empty(max(rd.library().rd_forward_workspace_size(m, h, d_out, d["G"], 0), 16), dtype=torch.uint8,
+                      device="cuda")
 
     def layer():
         rd.ragged_dot(d["x"], d["w"], gs, out=o, workspace=ws)
         rd.glu_fwd(o, out=act)
+        rd.ragged_dot(act, wo, gs, out=out, workspace=ws2)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -348,17 +354,28 @@ def decode_graph(d, ws, steps, warmup):
             evs[i - warmup][1].record(stream)
     torch.cuda.synchronize()
     t = sorted(a.elapsed_time(b) for a, b in evs)
-    got = act.clone()
+    got = out.clone()
     last = gs_b if (warmup + steps - 1) % 2 else gs_a
     gs.copy_(last)
     layer()
     torch.cuda.synchronize()
-    if not torch.equal(got.view(torch.int16), act.view(torch.int16)):
+    if not torch.equal(got.view(torch.int16), out.view(torch.int16)):
         raise RuntimeError("decode graph replay differs from the eager layer")
     q = lambda f: t[min(len(t) - 1, int(round(f * (len(t) - 1))))]
-    return {"ms": round(sum(t) / len(t), 4), "p10_p50_p90_ms": [round(q(0.1), 4), round(q(0.5), 4), round(q(0.9), 4)],
-            "timing": "replays of one captured graph (ragged_dot -> GLU), group_sizes rewritten on the device "
-                      "between replays (outside the events); last replay checked bitwise against eager"}
+    ms = sum(t) / len(t)
+    # algorithmic bytes of the replays' two size vectors (averaged): x, the weights of non-empty experts of
+    # wi and wo, the [gate | up] buffer written and read, act written and read, the output
+    nb = 0
+    for g in (gs_a, gs_b):
+        sz = g.cpu().numpy()
+        rows, nz = int(sz.sum()), int((sz > 0).sum())
+        nb += (rows * d["k"] * 2 + nz * d["k"] * n * 2 + 2 * rows * n * 2 + 2 * rows * h * 2 + nz * h * d_out * 2
+               + rows * d_out * 2) / 2
+    return {"ms": round(ms, 4), "p10_p50_p90_ms": [round(q(0.1), 4), round(q(0.5), 4), round(q(0.9), 4)],
+            "GB/s": round(nb / ms / 1e6, 1), "hbm_frac": round(nb / ms / 1e6 / HBM_PEAK_GBS, 4),
+            "timing": "replays of one captured graph (wi ragged_dot -> GLU -> wo ragged_dot), group_sizes "
+                      "rewritten on the device between replays (outside the events); last replay checked "
+                      "bitwise against eager"}
 
 
 def extra_all(steps):
@@ -434,6 +451,16 @@ def extra_all(steps):
     ms = per["window_ragged_dot"]
     out["window_limit_ragged_dot"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1),
                                       "GB/s": round(nb / ms / 1e6, 1)}
+    # the same forward with the heaviest ranks of Zipf(1.1) sizes inside the window (a hot window)
+    hs = workloads.hot_window_sizes()
+    gsh = torch.tensor(hs, dtype=torch.int32, device="cuda")
+    _, _, per_h = timed_ops([("hot", lambda: rd.ragged_dot(d["x"], d["w"], gsh, off, lim, out=o))], steps, 3)
+    hrows = int(hs[96:128].astype("int64").sum())
+    flh = 2.0 * hrows * d["k"] * d["n"]
+    out["window_limit_ragged_dot_hot_window"] = {
+        "ms": round(per_h["hot"], 4), "TFLOP/s": round(flh / per_h["hot"] / 1e9, 1),
+        "mfma_frac": round(flh / per_h["hot"] / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4), "window_rows": hrows,
+        "sizes": "Zipf(1.1) over 256 groups, the 32 heaviest ranks in the window 96..127"}
     tr = measured_traffic(PACKED_TRAFFIC_FILE)
     for key, nbytes in (("glu_fwd", L * h * 6), ("glu_bwd", L * h * 10)):
         out[f"window_limit_{key}"] = {"ms": round(per[key], 4), "GB/s": round(nbytes / per[key] / 1e6, 1),
@@ -731,8 +758,8 @@ def sweep(steps):
 
 def profile_run(which, steps, warmup, cold=False, settle_steps=0):
     """One workload's kernels and nothing else (no timing, no oracle), for rocprofv3 runs; with cold, the
-    caches are flushed before every pass as in the headline's timing; settle_steps untimed passes (no
-    flushes) come first, as before the headline's timed loops."""
+    caches are flushed before every pass as in the headline's timing; settle_steps untimed passes (flushed
+    too, with cold) come first, as before the headline's timed loops."""
     import torch
 
     from expert_ffn_ragged_amd import rd, workloads

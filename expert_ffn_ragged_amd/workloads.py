@@ -86,6 +86,20 @@ def hot_expert_sizes(total=32768, hot_rows=19660, hot=5, G=64, s=1.1, seed=11):
     return np.concatenate([rest[:hot], [hot_rows], rest[hot:]]).astype(np.int32)
 
 
+def hot_window_sizes(G=256, total=126156, lo=96, hi=128, s=1.1, seed=44):
+    """The packed buffer's valid rows over G groups with Zipf(s) shares whose heaviest hi - lo ranks sit
+    in the window [lo, hi) (in a seeded order), the other ranks on the other groups."""
+    rng = np.random.default_rng(seed)
+    p = np.arange(1, G + 1, dtype=np.float64) ** (-s)
+    p /= p.sum()
+    inside = lo + rng.permutation(hi - lo)
+    outside = np.concatenate([np.arange(0, lo), np.arange(hi, G)])[rng.permutation(G - (hi - lo))]
+    probs = np.empty(G, dtype=np.float64)
+    probs[inside] = p[:hi - lo]
+    probs[outside] = p[hi - lo:]
+    return multinomial_sizes(total, probs, rng)
+
+
 def random_sizes(G, total, seed, empty=()):
     """Uniform multinomial sizes with the listed groups forced empty (for sweeps)."""
     rng = np.random.default_rng(seed)
