@@ -161,6 +161,29 @@ def test_unsort_rejects_bad_arguments(lib):
     assert call(rows=0, g=None, y=None, w=None, grad=None, dot=None) == rd.RD_OK
 
 
+def test_zero_rows_from_limit_checks_arguments_before_launch(lib):
+    """rd_zero_rows_from_limit: sizes and pointers are checked on the host; the cases that launch
+    nothing (no rows, no limit) return OK without touching the GPU."""
+    v = ctypes.c_void_p
+    ok = dict(buf=16, limit=16, rows=4, row_bytes=32)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        p = lambda x: None if x is None else v(x)
+        return lib.rd_zero_rows_from_limit(p(a["buf"]), p(a["limit"]), a["rows"], a["row_bytes"], None)
+    assert call(rows=-1) == rd.RD_EINVAL
+    assert call(row_bytes=0) == rd.RD_EINVAL
+    assert call(row_bytes=-16) == rd.RD_EINVAL
+    assert call(row_bytes=24) == rd.RD_EUNSUPPORTED    # not whole 16-byte vectors
+    assert call(rows=1 << 40, row_bytes=1 << 30) == rd.RD_EUNSUPPORTED  # rows x row_bytes past 2^62
+    assert call(buf=None) == rd.RD_EINVAL
+    assert call(buf=24) == rd.RD_EINVAL               # misaligned buffer
+    assert call(limit=18) == rd.RD_EINVAL             # misaligned int32
+    assert call(rows=0, buf=None, limit=None) == rd.RD_OK
+    assert call(limit=None) == rd.RD_OK               # no limit: every row is below it
+
+
 def test_forward_glu_rejects_bad_arguments(lib):
     """The fused up-projection + GLU: shape rules (k % 64, h % 128) and pointers, checked before launch."""
     v = ctypes.c_void_p
