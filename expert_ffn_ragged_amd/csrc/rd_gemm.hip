@@ -1300,31 +1300,6 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
   const int wm_off = (wave / WC) * WM, wn_off = (wave % WC) * WN;
   const Window win = build_local_bounds<NT>(p.gs, p.G, p.offp, p.gl, p.limp, p.m, s_lb, s_wave);
 
-  // Rows below the limit outside the window are written as +0 while the
-  // tiles run: the rows [0, lo) and [hi, L) form two contiguous ranges, cut
-  // into 1 KB chunks (64 lanes x 16 B) dealt round-robin over every wave of
-  // the grid.  Each wave stores one chunk per contraction step, before the
-  // step's loads, so the next step's load wait also covers it (loads
-  // complete in order among themselves, so the wait's count stays right);
-  // the rest go out after the wave's last tile.  The stores share the
-  // vector-memory path with the loads, so the overlap is partial: the
-  // window+limit forward went from 236 to 227 us.  The fused-GLU tile keeps
-  // the zeroing after its tiles (it also zeroes its second output).
-  constexpr bool kZil = !is_trans(MODE) && MODE != kFwdGLU;
-  const long long z_row = static_cast<long long>(p.n) * (p.out_f32 ? 4 : 2);
-  const long long z_v1 = static_cast<long long>(win.lo) * (z_row / 16);
-  const long long z_v = z_v1 + static_cast<long long>(win.L - win.hi) * (z_row / 16);
-  const long long z_end = (z_v + 63) / 64;
-  const long long z_stride = static_cast<long long>(gridDim.x) * NW;
-  long long z_next = static_cast<long long>(blockIdx.x) * NW + wave;
-  auto zero_chunk = [&]() {
-    const long long q = z_next * 64 + (threadIdx.x & 63);
-    if (q < z_v) {
-      char* dst = static_cast<char*>(p.out) + (q < z_v1 ? q * 16 : static_cast<long long>(win.hi) * z_row + (q - z_v1) * 16);
-      store16<true>(u32x4_t{0, 0, 0, 0}, dst);
-    }
-    z_next += z_stride;
-  };
   Tiles tl;
   if constexpr (is_trans(MODE)) {
     order_groups<NT>(s_lb, p.gl, s_aux);
@@ -1433,18 +1408,12 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
       __builtin_amdgcn_sched_barrier(0);
       const uint16_t* slot = s_tiles + (g % S) * ST;
       if constexpr (is_fp8(MODE)) {
-        if constexpr (kZil)
-          if (z_next < z_end) zero_chunk();
-        __builtin_amdgcn_sched_barrier(0);
         produce();
         __builtin_amdgcn_sched_barrier(0);
         mma_stage8<OpA, OpB, MI, NI, KS>(slot, slot + A_EL, acc, wm_off, wn_off);
       } else {
         StageFrags<OpA, OpB, MI, NI> fr;
         stage_frags(slot, slot + A_EL, fr, wm_off, wn_off);
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (kZil)
-          if (z_next < z_end) zero_chunk();
         __builtin_amdgcn_sched_barrier(0);
         produce();
         __builtin_amdgcn_sched_barrier(0);
@@ -1462,11 +1431,7 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
       store_wave_tile<MI, NI, EPI, 0, NI, kNtStores, is_trans(MODE), EPI16>(acc, out, of32, ld, r0, rlim, c0, clim,
                                                                             stage);
   }
-  if constexpr (kZil) {
-    while (z_next < z_end) zero_chunk();
-  } else if constexpr (!is_trans(MODE)) {
-    zero_outside_window<NT>(p.out, p.n, p.out_f32 != 0, win);
-  }
+  if constexpr (!is_trans(MODE)) zero_outside_window<NT>(p.out, p.n, p.out_f32 != 0, win);
   if constexpr (MODE == kFwdGLU)
     if (p.out2 != nullptr) zero_outside_window<NT>(p.out2, 2 * p.n, false, win);
 }
