@@ -1258,7 +1258,47 @@ struct StreamOps<kFwdGLU, BM, BN, KS, NW> {
 // fits).  The workgroup is WR x WC waves (each owns a BM/WR x BN/WC block of
 // the tile): 2 x 2, or 8 waves (two per SIMD, so one wave's MFMAs issue
 // while the other waits on a barrier or an LDS read).
-template <int MODE, int BM, int BN, int S, int KS, int WGS, int MAXL = RD_MAX_GROUPS, int WR = 2, int WC = 2>
+// The zero rows of a window, written by the forward tiles while they run
+// (the ZIL instance of grouped_gemm_stream; see there).  One wave's share:
+// 1 KB chunks (64 lanes x 16 B) of the two contiguous ranges [0, lo) and
+// [hi, L), every (grid waves)-th chunk from the wave's global index.  The
+// false specialisation holds nothing, so the other instances compile as if
+// it were not there.
+template <bool ON>
+struct WindowZeros {
+  __device__ WindowZeros(const KArgs&, const Window&, int, int) {}
+};
+template <>
+struct WindowZeros<true> {
+  char* out;
+  long long row, v1, v, next, end, stride, hi_off;
+  __device__ WindowZeros(const KArgs& p, const Window& win, int nw, int wave) {
+    out = static_cast<char*>(p.out);
+    row = static_cast<long long>(p.n) * (p.out_f32 ? 4 : 2);
+    v1 = static_cast<long long>(win.lo) * (row / 16);
+    v = v1 + static_cast<long long>(win.L - win.hi) * (row / 16);
+    end = (v + 63) / 64;
+    stride = static_cast<long long>(gridDim.x) * nw;
+    next = static_cast<long long>(blockIdx.x) * nw + wave;
+    hi_off = static_cast<long long>(win.hi) * row;
+  }
+  __device__ __forceinline__ void chunk() {
+    const long long q = next * 64 + (threadIdx.x & 63);
+    if (q < v) store16<true>(u32x4_t{0, 0, 0, 0}, out + (q < v1 ? q * 16 : hi_off + (q - v1) * 16));
+    next += stride;
+  }
+  // one chunk per contraction step, before the step's loads
+  __device__ __forceinline__ void step() {
+    if (next < end) chunk();
+  }
+  // what is left after the wave's last tile
+  __device__ __forceinline__ void drain() {
+    while (next < end) chunk();
+  }
+};
+
+template <int MODE, int BM, int BN, int S, int KS, int WGS, int MAXL = RD_MAX_GROUPS, int WR = 2, int WC = 2,
+          bool ZIL = false>
 __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p) {
   constexpr int NW = WR * WC, NT = NW * 64;
   constexpr int WM = BM / WR, WN = BN / WC;
@@ -1300,6 +1340,19 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
   const int wm_off = (wave / WC) * WM, wn_off = (wave % WC) * WN;
   const Window win = build_local_bounds<NT>(p.gs, p.G, p.offp, p.gl, p.limp, p.m, s_lb, s_wave);
 
+  // ZIL (forward tiles of calls with a window): rows below the limit
+  // outside the window are written as +0 while the tiles run.  The rows
+  // [0, lo) and [hi, L) form two contiguous ranges, cut into 1 KB chunks (64
+  // lanes x 16 B) dealt round-robin over every wave of the grid; each wave
+  // stores one chunk per contraction step, before the step's loads, so the
+  // next step's load wait also covers it (loads complete in order among
+  // themselves, so the wait's count stays right), and the rest after its
+  // last tile.  The stores share the vector-memory path with the loads, so
+  // the overlap is partial (the window+limit forward: 236 -> 225 us).  A
+  // separate instance: the chunk state costs the other forward tiles SGPR
+  // spills in their loop.
+  constexpr bool kZil = ZIL && (MODE == kFwdNN || MODE == kFwdNT);
+  WindowZeros<kZil> zeros(p, win, NW, wave);
   Tiles tl;
   if constexpr (is_trans(MODE)) {
     order_groups<NT>(s_lb, p.gl, s_aux);
@@ -1415,6 +1468,10 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
         StageFrags<OpA, OpB, MI, NI> fr;
         stage_frags(slot, slot + A_EL, fr, wm_off, wn_off);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kZil) {
+          zeros.step();
+          __builtin_amdgcn_sched_barrier(0);
+        }
         produce();
         __builtin_amdgcn_sched_barrier(0);
         mma_stage<OpA, OpB, MI, NI, KS>(slot, slot + A_EL, fr, acc, wm_off, wn_off);
@@ -1431,7 +1488,11 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
       store_wave_tile<MI, NI, EPI, 0, NI, kNtStores, is_trans(MODE), EPI16>(acc, out, of32, ld, r0, rlim, c0, clim,
                                                                             stage);
   }
-  if constexpr (!is_trans(MODE)) zero_outside_window<NT>(p.out, p.n, p.out_f32 != 0, win);
+  if constexpr (kZil) {
+    zeros.drain();
+  } else if constexpr (!is_trans(MODE)) {
+    zero_outside_window<NT>(p.out, p.n, p.out_f32 != 0, win);
+  }
   if constexpr (MODE == kFwdGLU)
     if (p.out2 != nullptr) zero_outside_window<NT>(p.out2, 2 * p.n, false, win);
 }
@@ -2019,22 +2080,22 @@ KArgs with_per_cu(KArgs a, int grid) {
 }
 
 template <int MODE, int BM, int BN, int S, int KS = 32, int WGS = 1, int MAXL = RD_MAX_GROUPS, int WR = 2,
-          int WC = 2>
+          int WC = 2, bool ZIL = false>
 void launch_one(const KArgs& a, long long work, hipStream_t stream) {
   if constexpr (S == 0)
     grouped_gemm_regs<MODE, BM, BN><<<grid_size(work, 2), kThreads, 0, stream>>>(a);
   else
-    grouped_gemm_stream<MODE, BM, BN, S, KS, WGS, MAXL, WR, WC><<<grid_size(work, WGS), WR * WC * 64, 0, stream>>>(
-        with_per_cu(a, grid_size(work, WGS)));
+    grouped_gemm_stream<MODE, BM, BN, S, KS, WGS, MAXL, WR, WC, ZIL>
+        <<<grid_size(work, WGS), WR * WC * 64, 0, stream>>>(with_per_cu(a, grid_size(work, WGS)));
 }
 
 // launch_one for tile shape TILE, checked against kTileShapes (which sizes the trans workspace).
 template <int TILE, int MODE, int BM, int BN, int S, int KS = 32, int WGS = 1, int MAXL = RD_MAX_GROUPS, int WR = 2,
-          int WC = 2>
+          int WC = 2, bool ZIL = false>
 void launch_checked(const KArgs& a, long long work, hipStream_t stream) {
   static_assert(kTileShapes[TILE].bm == BM && kTileShapes[TILE].bn == BN && kTileShapes[TILE].wgs == WGS,
                 "kTileShapes must match the launched shape");
-  launch_one<MODE, BM, BN, S, KS, WGS, MAXL, WR, WC>(a, work, stream);
+  launch_one<MODE, BM, BN, S, KS, WGS, MAXL, WR, WC, ZIL>(a, work, stream);
 }
 
 template <int MODE, int S, int KS>
@@ -2042,8 +2103,10 @@ void launch_pp(const KArgs& a, long long work, hipStream_t stream) {
   grouped_gemm_pp<MODE, S, KS><<<grid_size(work, 1), 512, 0, stream>>>(a);
 }
 
+// zil: the call has a window, whose zero rows the kW128x256 forward tile
+// writes while its tiles run (the ZIL instance of grouped_gemm_stream).
 template <int MODE>
-void launch_tile(int tile, const KArgs& a, const GemmProblem& p, hipStream_t stream) {
+void launch_tile(int tile, const KArgs& a, const GemmProblem& p, hipStream_t stream, bool zil = false) {
   auto work = [&](int BM, int BN) {
     if (is_trans(MODE))
       return static_cast<long long>(p.num_local) * ((p.k + BM - 1) / BM) * ((p.n + BN - 1) / BN);
@@ -2074,7 +2137,14 @@ void launch_tile(int tile, const KArgs& a, const GemmProblem& p, hipStream_t str
     // eight waves (two per SIMD) sharing one ring: 4 x 2 waves of 64 x 128,
     // 2 x 4 waves of 64 x 64, and the 256 x 256 tile with 64-deep stages
     case kW256x256: launch_checked<kW256x256, MODE, 256, 256, 4, 32, 1, RD_MAX_GROUPS, 4, 2>(a, work(256, 256), stream); break;
-    case kW128x256: launch_checked<kW128x256, MODE, 128, 256, 3, 64, 1, RD_MAX_GROUPS, 2, 4>(a, work(128, 256), stream); break;
+    case kW128x256:
+      if constexpr (MODE == kFwdNN || MODE == kFwdNT)
+        if (zil) {
+          launch_checked<kW128x256, MODE, 128, 256, 3, 64, 1, RD_MAX_GROUPS, 2, 4, true>(a, work(128, 256), stream);
+          break;
+        }
+      launch_checked<kW128x256, MODE, 128, 256, 3, 64, 1, RD_MAX_GROUPS, 2, 4>(a, work(128, 256), stream);
+      break;
     case kW256x256k64: launch_checked<kW256x256k64, MODE, 256, 256, 2, 64, 1, RD_MAX_GROUPS, 4, 2>(a, work(256, 256), stream); break;
     case kW128x512: launch_checked<kW128x512, MODE, 128, 512, 3, 32, 1, RD_MAX_GROUPS, 2, 4>(a, work(128, 512), stream); break;
     case kW128x256k32: launch_checked<kW128x256k32, MODE, 128, 256, 6, 32, 1, RD_MAX_GROUPS, 2, 4>(a, work(128, 256), stream); break;
@@ -2190,10 +2260,11 @@ int launch_forward(const GemmProblem& p, bool trans_rhs, void* workspace, size_t
   const bool dma = (p.k % BK) == 0 && fits_32bit(p.m, p.k) && fits_32bit(p.k, p.n);
   if (dma) {
     const int tile = pick_forward_tile(p, trans_rhs);
+    const bool zil = p.group_offset != nullptr;  // a window: rows outside it are zeroed
     if (trans_rhs)
-      launch_tile<kFwdNT>(tile, a, p, stream);
+      launch_tile<kFwdNT>(tile, a, p, stream, zil);
     else
-      launch_tile<kFwdNN>(tile, a, p, stream);
+      launch_tile<kFwdNN>(tile, a, p, stream, zil);
   } else {
     const long long work = (static_cast<long long>((p.m + 127) / 128) + p.num_local) * ((p.n + 127) / 128) +
                            (p.m + kZeroRows - 1) / kZeroRows + 2;
