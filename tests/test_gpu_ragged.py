@@ -109,6 +109,22 @@ def test_every_window_offset(off, trans_rhs):
     check_forward_full(x, w, gs_host, off, None, trans_rhs, o32, o16, f"off={off}")
 
 
+@pytest.mark.parametrize("trans_rhs", [False, True])
+@pytest.mark.parametrize("off,limit", [(2, None), (0, 2100), (5, 3000), (3, 400), (7, None)])
+def test_window_zero_rows_while_tiles_run(off, limit, trans_rhs):
+    """The 128 x 256 eight-wave forward tile with a window writes the rows outside it (below the
+    limit) as +0 in 1 KB chunks between its contraction steps.  Forced tile, n = 520 so that the
+    chunks straddle rows (1040 B bf16 rows, 2080 B float32), limits inside, before and after the
+    window, and rows past the sizes."""
+    say(f"window zero rows on the wide tile: off={off} limit={limit} trans_rhs={trans_rhs}")
+    gs_host = np.array([300, 0, 450, 120, 610, 33, 0, 280, 500, 95], dtype=np.int32)
+    m, k, n, gl = int(gs_host.sum()) + 300, 256, 520, 3
+    x, w, gs = _case(m, k, n, gs_host, gl, 40 + off, trans_rhs)
+    with rd.tuning(fwd_tile=14):
+        o32, o16 = run_forward(x, w, gs, off=off, limit=limit, trans_rhs=trans_rhs)
+    check_forward_full(x, w, gs_host, off, limit, trans_rhs, o32, o16, f"off={off} limit={limit}")
+
+
 @pytest.mark.parametrize("off", [-1, 5, 7, 1 << 30])
 def test_window_that_does_not_fit_is_all_zero(off):
     say(f"invalid window off={off}")
