@@ -210,7 +210,8 @@ size_t rd_trans_workspace_size(int64_t m, int64_t k, int64_t n, int32_t num_loca
 
 int rd_trans_fp8(const void* x, const void* dy, const int32_t* group_sizes, int32_t num_groups,
                  const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* dw,
-                 int32_t dw_dtype, int64_t m, int64_t k, int64_t n, void* stream) {
+                 int32_t dw_dtype, int64_t m, int64_t k, int64_t n, void* workspace, size_t workspace_bytes,
+                 void* stream) {
   int st = check_dims(m, k, n);
   if (st != RD_OK) return st;
   if ((k % 16) != 0 || (n % 16) != 0) return RD_EUNSUPPORTED;
@@ -224,6 +225,7 @@ int rd_trans_fp8(const void* x, const void* dy, const int32_t* group_sizes, int3
   if ((reinterpret_cast<uintptr_t>(group_sizes) & 3u) || (reinterpret_cast<uintptr_t>(limit) & 3u) ||
       (reinterpret_cast<uintptr_t>(group_offset) & 3u))
     return RD_EINVAL;
+  if (workspace_bytes > 0 && (workspace == nullptr || !aligned16(workspace))) return RD_EINVAL;
   rd::GemmProblem p{};
   p.a = x;
   p.b = dy;
@@ -237,7 +239,8 @@ int rd_trans_fp8(const void* x, const void* dy, const int32_t* group_sizes, int3
   p.m = static_cast<int>(m);
   p.k = static_cast<int>(k);
   p.n = static_cast<int>(n);
-  return rd::launch_trans_fp8(p, static_cast<hipStream_t>(stream));
+  return rd::launch_trans_fp8(p, workspace_bytes > 0 ? workspace : nullptr, workspace_bytes,
+                              static_cast<hipStream_t>(stream));
 }
 
 int rd_trans(const void* x, const void* dy, const int32_t* group_sizes, int32_t num_groups,

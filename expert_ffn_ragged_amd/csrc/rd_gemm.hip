@@ -837,11 +837,15 @@ struct TransTiles {
   // share a CU): below that, the CU holding it also runs lighter work of its
   // co-resident workgroups, and the partials' round trip through memory costs
   // more than the balance gains (measured on the 32768-row backward, whose
-  // largest expert is 0.57 of that mean: 362 us unsplit, 386 us split).  At
+  // largest expert is 0.57 of that mean: 362 us unsplit, 386 us split).
+  // F10 / 10 scales that threshold: 1 for bf16, 1.3 for fp8 operands, whose
+  // tiles take half the steps for the same partial traffic (one expert
+  // holding 60 % of the backward's rows, 1.13 of the mean: 212 us unsplit,
+  // 231 us split; 80 %, 1.5 of it: 242 vs 232 us; 95 %: 279 vs 234 us).  At
   // most cap_tiles partial tiles (the workspace); fewer split groups when
   // they would not fit.  Workgroup 0 writes the plan to the workspace header
   // for the reduction.  NT threads; ends with a barrier.
-  template <int NT, int KS>
+  template <int NT, int KS, int F10 = 10>
   __device__ void plan(const int* s_lb, const int* s_order, int gl, long long* s_wave, int* s_cp, long long cap_tiles,
                        int per_cu, int* header) {
     long long mine = 0;
@@ -858,7 +862,7 @@ struct TransTiles {
       const long long tiles = static_cast<long long>(ka) * nc;
       while (n < kMaxSplit && n < gl) {
         const long long st = steps_at<KS>(s_lb, s_order, n);
-        if (st * G < total * per_cu || st <= c) break;
+        if (st * G * 10 < total * per_cu * F10 || st <= c) break;
         const int P = static_cast<int>((st + c - 1) / c);
         if ((cp + P) * tiles > cap_tiles) break;
         cp += P;
@@ -1357,7 +1361,7 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
   if constexpr (is_trans(MODE)) {
     order_groups<NT>(s_lb, p.gl, s_aux);
     tl.init(p.gl, p.k, p.n, BM, BN);
-    if (MODE == kTransTN && p.ws != nullptr) {
+    if ((MODE == kTransTN || MODE == kTransTN8) && p.ws != nullptr) {
       const long long part_bytes = static_cast<long long>(BM) * BN * 4;
       const long long cap = (p.ws_bytes - kSplitHeaderInts * 4) / part_bytes;
       int* header = static_cast<int*>(p.ws);
@@ -1365,8 +1369,8 @@ __global__ __launch_bounds__(WR * WC * 64, WGS) void grouped_gemm_stream(KArgs p
         header[1] = BM;
         header[2] = BN;
       }
-      tl.template plan<NT, KSTEP>(s_lb, s_aux, p.gl, s_wave, s_cp, cap > 0 ? cap : 0, p.per_cu > 0 ? p.per_cu : 1,
-                                  header);
+      tl.template plan<NT, KSTEP, MODE == kTransTN8 ? 13 : 10>(s_lb, s_aux, p.gl, s_wave, s_cp, cap > 0 ? cap : 0,
+                                                               p.per_cu > 0 ? p.per_cu : 1, header);
     }
   } else {
     const int total_m = tile_prefix<NT>(s_lb, p.gl, BM, s_aux, s_wave);
@@ -2340,9 +2344,16 @@ int launch_forward_fp8(const GemmProblem& p, bool trans_rhs, hipStream_t stream)
   return hipGetLastError() == hipSuccess ? RD_OK : RD_EHIP;
 }
 
-int launch_trans_fp8(const GemmProblem& p, hipStream_t stream) {
-  const KArgs a = make_args(p);
+int launch_trans_fp8(const GemmProblem& p, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  KArgs a = make_args(p);
   const long long tiles = static_cast<long long>(p.num_local) * ((p.k + 127) / 128) * ((p.n + 255) / 256);
+  // the row split of long groups as for bf16 (same 128 x 256 tiles, the
+  // same workspace header and partial layout, the same reduction)
+  const bool split = workspace != nullptr && workspace_bytes > kSplitHeaderInts * 4;
+  if (split) {
+    a.ws = workspace;
+    a.ws_bytes = static_cast<long long>(workspace_bytes);
+  }
   // two co-resident workgroups per CU with 3-slot rings of 64-row stages (one
   // multiplies while the other drains its dW stores), as for bf16; measured
   // 317 -> 232 us at the backward shape (m32768, k1024, n4096)
@@ -2350,6 +2361,10 @@ int launch_trans_fp8(const GemmProblem& p, hipStream_t stream) {
     launch_one<kTransTN8, 128, 256, 3, 32, 2, 512>(a, tiles, stream);
   else
     launch_one<kTransTN8, 128, 256, 3, 64>(a, tiles, stream);
+  if (split)
+    trans_split_reduce<<<grid_size(static_cast<long long>(p.k) * (p.n / 8) / kReduceThreads + 1, 1), kReduceThreads, 0,
+                         stream>>>(static_cast<const int*>(workspace), static_cast<long long>(workspace_bytes), p.out,
+                                   p.out_f32 ? 1 : 0, p.k, p.n, p.num_local);
   return hipGetLastError() == hipSuccess ? RD_OK : RD_EHIP;
 }
 

@@ -47,7 +47,7 @@ int launch_forward_noalloc(const GemmProblem& p, hipStream_t stream);
 // n % 16 == 0 and k * max(m, n) < 2^32.
 int launch_forward_fp8(const GemmProblem& p, bool trans_rhs, hipStream_t stream);
 // fp8 x [m, k] and dy [m, n]; requires k % 16 == 0, n % 16 == 0, m * max(k, n) < 2^32.
-int launch_trans_fp8(const GemmProblem& p, hipStream_t stream);
+int launch_trans_fp8(const GemmProblem& p, void* workspace, size_t workspace_bytes, hipStream_t stream);
 // ragged_dot(x, w) with the GLU as its epilogue; requires k % 64 == 0, n (= h) % 128 == 0 and
 // operands under 4 GiB (fused_glu_supported).
 bool fused_glu_supported(const GemmProblem& p);

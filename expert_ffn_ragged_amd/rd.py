@@ -19,7 +19,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librd.so")
 
-ABI_VERSION = 7
+ABI_VERSION = 8
 RD_OK, RD_EINVAL, RD_EUNSUPPORTED, RD_EHIP, RD_ESCRATCH = 0, 1, 2, 3, 4
 RD_NOALLOC_SCRATCH_BYTES = 80 << 20
 RD_BF16, RD_F32 = 0, 1
@@ -84,7 +84,7 @@ def library():
     lib.rd_trans_workspace_size.argtypes = [i64, i64, i64, i32]
     lib.rd_trans.restype = ctypes.c_int
     lib.rd_trans.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, i32, i64, i64, i64, vp, sz, vp]
-    lib.rd_trans_fp8.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, i32, i64, i64, i64, vp]
+    lib.rd_trans_fp8.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, i32, i64, i64, i64, vp, sz, vp]
     lib.rd_glu_fwd.restype = ctypes.c_int
     lib.rd_glu_fwd.argtypes = [vp, vp, vp, i64, i64, vp]
     lib.rd_glu_bwd.restype = ctypes.c_int
@@ -275,10 +275,11 @@ def ragged_dot_fp8(x, w, group_sizes, group_offset=None, limit=None, trans_rhs=F
 
 
 def trans_ragged_dot_fp8(x, dy, group_sizes, num_local=None, group_offset=None, limit=None,
-                         out_dtype=torch.float32, out=None, stream=None):
+                         out_dtype=torch.float32, out=None, workspace=None, row_split=True, stream=None):
     """fp8 (E4M3) trans_ragged_dot: dw[j] = x_j^T @ dy_j, float32 accumulation, one rounding to out_dtype.
 
-    x: [m, k] and dy: [m, n] torch.float8_e4m3fn; returns [num_local, k, n].
+    x: [m, k] and dy: [m, n] torch.float8_e4m3fn; returns [num_local, k, n].  ``workspace`` and
+    ``row_split`` as for trans_ragged_dot (the same row split of long groups).
     """
     _need(x, "x", torch.float8_e4m3fn, 2)
     _need(dy, "dy", torch.float8_e4m3fn, 2)
@@ -296,8 +297,19 @@ def trans_ragged_dot_fp8(x, dy, group_sizes, num_local=None, group_offset=None, 
     _need(out, "out", out.dtype, 3)
     if tuple(out.shape) != (gl, k, n) or out.dtype not in _DTYPES:
         raise ValueError("out must be [num_local, k, n] bf16 or float32")
-    _check(library().rd_trans_fp8(_ptr(x), _ptr(dy), _ptr(group_sizes), group_sizes.numel(), _ptr(group_offset), gl,
-                                  _ptr(limit), _ptr(out), _DTYPES[out.dtype], m, k, n, _stream(stream)))
+    lib = library()
+    ws_bytes = 0
+    if row_split and workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1)
+        ws_bytes = workspace.numel()
+    elif row_split:
+        ws_bytes = lib.rd_trans_workspace_size(m, k, n, gl)
+        if ws_bytes:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+            _on_stream(stream, workspace)
+    _check(lib.rd_trans_fp8(_ptr(x), _ptr(dy), _ptr(group_sizes), group_sizes.numel(), _ptr(group_offset), gl,
+                            _ptr(limit), _ptr(out), _DTYPES[out.dtype], m, k, n,
+                            _ptr(workspace) if ws_bytes else None, ws_bytes, _stream(stream)))
     return out
 
 

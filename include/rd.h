@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define RD_ABI_VERSION 7
+#define RD_ABI_VERSION 8
 
 /* status codes */
 #define RD_OK 0
@@ -229,11 +229,16 @@ int rd_trans(const void* x, const void* dy, const int32_t* group_sizes, int32_t 
  * products over the group's rows, one rounding to dw_dtype; rows outside a
  * group removed by selection, an empty group +0, rows >= L never read.
  * Requires k and n multiples of 16 and m * max(k, n) < 2^32 (else
- * RD_EUNSUPPORTED).  No workspace.
+ * RD_EUNSUPPORTED).  workspace/workspace_bytes as for rd_trans, with the
+ * same row split of long groups (fp32 partials added in chunk order, the
+ * same determinism); rd_trans_workspace_size(m, k, n, num_local) bytes let
+ * every qualifying group split (0 from it: no split).  RD_EINVAL for
+ * workspace_bytes > 0 with a NULL or misaligned workspace.
  */
 int rd_trans_fp8(const void* x, const void* dy, const int32_t* group_sizes, int32_t num_groups,
                  const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* dw,
-                 int32_t dw_dtype, int64_t m, int64_t k, int64_t n, void* stream);
+                 int32_t dw_dtype, int64_t m, int64_t k, int64_t n, void* workspace, size_t workspace_bytes,
+                 void* stream);
 
 /*
  * The MoE up-projection with the GLU as its epilogue ([MaxText]: the expert

@@ -46,7 +46,7 @@ def test_links_the_same_hip_runtime_soname_as_torch():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.rd_abi_version() == rd.ABI_VERSION == 7
+    assert lib.rd_abi_version() == rd.ABI_VERSION == 8
     for s in (0, 1, 2, 3, 99):
         assert isinstance(lib.rd_status_string(s), bytes)
 
@@ -218,6 +218,21 @@ def test_fp8_forms_reject_bad_sizes(lib):
         assert call(fn, k=0) == rd.RD_EINVAL
         assert call(fn, m=0) == rd.RD_OK
     assert call(lib.rd_forward_fp8, n=24) == rd.RD_EUNSUPPORTED
+
+
+def test_trans_fp8_rejects_bad_arguments(lib):
+    """fp8 trans_ragged_dot: k and n multiples of 16, the output dtype, and the row-split workspace
+    rules of rd_trans (a size needs a 16-byte aligned pointer), before any launch."""
+    v = ctypes.c_void_p
+
+    def call(k=32, n=32, ws=None, ws_bytes=0, dt=0):
+        p = lambda x: None if x is None else v(x)
+        return lib.rd_trans_fp8(v(16), v(16), v(16), 4, None, 4, None, v(16), dt, 8, k, n, p(ws), ws_bytes, None)
+    assert call(k=24) == rd.RD_EUNSUPPORTED
+    assert call(n=40) == rd.RD_EUNSUPPORTED
+    assert call(dt=7) == rd.RD_EINVAL
+    assert call(ws=None, ws_bytes=4096) == rd.RD_EINVAL
+    assert call(ws=24, ws_bytes=4096) == rd.RD_EINVAL
 
 
 def test_tuning_hook_validates_and_restores(lib):

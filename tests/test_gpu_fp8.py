@@ -162,3 +162,47 @@ def test_fp8_trans_backward_shape_sampled():
             continue
         ref = oracle.trans_ragged_dot_fp8(xc[r0:r1][:, a_rows], yc[r0:r1], np.array([r1 - r0], dtype=np.int32))[0]
         assert_gemm_close(got, ref, f"fp8 dW group {j}")
+
+
+SPLIT_CASES = [
+    # m, k, n, sizes, window (offset, num_local) or None, limit or None
+    (8192, 256, 512, [6000, 310, 0, 502, 377, 250, 400, 353], None, None),             # one long group
+    (9000, 256, 272, [100, 5000, 700, 900, 0, 600, 800, 300, 400, 200], (1, 8), 6500),  # window, limit in it
+]
+
+
+@pytest.mark.parametrize("case", range(len(SPLIT_CASES)))
+def test_fp8_trans_row_split(case):
+    """The row split of long groups on fp8 operands: the group is cut into row chunks (read back from the
+    workspace header), fp32 partials added in chunk order; every element against the oracle, NaN codes past
+    the valid rows kept out, bf16 = RNE(f32), a repeat bitwise equal, the unsplit result close."""
+    m, k, n, sizes, win, limit = SPLIT_CASES[case]
+    say(f"fp8 row split case {case}: m={m} k={k} n={n} sizes={sizes} window={win} limit={limit}")
+    gs_host = np.array(sizes, dtype=np.int32)
+    off, gl = (None, len(sizes)) if win is None else win
+    valid = int(min(gs_host.sum(), m if limit is None else limit))
+    x = fp8_normal((m, k), 1.0, 60 + case)
+    y = fp8_normal((m, n), 1.0, 70 + case)
+    x.view(torch.uint8)[valid:] = 0x7F
+    y.view(torch.uint8)[valid:] = 0x7F
+    gs = torch.from_numpy(gs_host).to(DEV)
+    offt = None if off is None else dev_i32(off)
+    limt = None if limit is None else dev_i32(limit)
+    ws = torch.zeros(rd.trans_workspace_size(m, k, n, gl), dtype=torch.uint8, device=DEV)
+    d32 = sentinel((gl, k, n), torch.float32)
+    d16 = sentinel((gl, k, n), torch.bfloat16)
+    rd.trans_ragged_dot_fp8(x, y, gs, gl, offt, limt, out=d32, workspace=ws)
+    torch.cuda.synchronize()
+    split_groups = int(ws[:4].view(torch.int32).item())
+    rd.trans_ragged_dot_fp8(x, y, gs, gl, offt, limt, out=d16, workspace=ws)
+    torch.cuda.synchronize()
+    assert split_groups > 0, f"case {case}: no group was split"
+    ref = oracle.trans_ragged_dot_fp8(codes(x), codes(y), gs_host, gl, off, limit)
+    assert_gemm_close(d32.cpu().numpy(), ref, f"fp8 split case {case}")
+    assert_bf16_is_rne_of_f32(d16, d32, f"fp8 split case {case}")
+    again = torch.empty_like(d32)
+    rd.trans_ragged_dot_fp8(x, y, gs, gl, offt, limt, out=again, workspace=ws)
+    plain = rd.trans_ragged_dot_fp8(x, y, gs, gl, offt, limt, row_split=False)
+    torch.cuda.synchronize()
+    assert torch.equal(again.view(torch.int32), d32.view(torch.int32)), f"case {case}: not deterministic"
+    assert_gemm_close(plain.cpu().numpy(), d32.cpu().numpy().astype(np.float64), f"fp8 case {case} vs unsplit")
