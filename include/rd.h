@@ -231,9 +231,11 @@ int rd_trans(const void* x, const void* dy, const int32_t* group_sizes, int32_t 
  * Requires k and n multiples of 16 and m * max(k, n) < 2^32 (else
  * RD_EUNSUPPORTED).  workspace/workspace_bytes as for rd_trans, with the
  * same row split of long groups (fp32 partials added in chunk order, the
- * same determinism); rd_trans_workspace_size(m, k, n, num_local) bytes let
- * every qualifying group split (0 from it: no split).  RD_EINVAL for
- * workspace_bytes > 0 with a NULL or misaligned workspace.
+ * same determinism), from 1.3 times the mean work per CU: these tiles take
+ * half the steps for the same partial traffic.
+ * rd_trans_workspace_size(m, k, n, num_local) bytes let every qualifying
+ * group split (0 from it: no split).  RD_EINVAL for workspace_bytes > 0 with
+ * a NULL or misaligned workspace.
  */
 int rd_trans_fp8(const void* x, const void* dy, const int32_t* group_sizes, int32_t num_groups,
                  const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* dw,
