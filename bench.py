@@ -34,6 +34,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, published (no sparsity)
 MFMA_FP8_PEAK_TFLOPS = 5033.2  # MI355X dense fp8 MFMA, published (no sparsity)
+# the hot expert's rows (of 32768) for the split / unsplit comparison beyond the default 60 %
+HOT_SHARES = (("80", 26214), ("95", 31130))
 METRIC = "ragged_dot TFLOP/s (valid rows) + % bf16 MFMA peak; decode-shape HBM GB/s"
 
 
@@ -412,6 +414,17 @@ def extra_all(steps):
     out["backward_m32768_hot_expert_dw"] = {
         key: {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1)} for key, ms in per_h.items()}
     out["backward_m32768_hot_expert_dw"]["sizes"] = "19660 rows in one expert, the rest Zipf(1.1) over 63"
+    # the same with 80 % and 95 % of the rows in the hot expert, split / unsplit (fp8 below)
+    shares = {"60": {key: round(ms, 4) for key, ms in per_h.items()}}
+    for pct, hot_rows in HOT_SHARES:
+        gsx = torch.tensor(workloads.hot_expert_sizes(hot_rows=hot_rows), dtype=torch.int32, device="cuda")
+        _, _, per_x = timed_ops([
+            ("split", lambda: rd.trans_ragged_dot(d["x"], d["dy"], gsx, out=dw)),
+            ("unsplit", lambda: rd.trans_ragged_dot(d["x"], d["dy"], gsx, out=dw, row_split=False)),
+        ], steps, 3)
+        shares[pct] = {key: round(ms, 4) for key, ms in per_x.items()}
+    hot_shares = {"unit": "ms", "rows_in_hot_expert": {"60": 19660, **{p: r for p, r in HOT_SHARES}},
+                  "bf16": shares}
     fld = 2.0 * m * k * n
     out["backward_m32768_dx_dense_torch_reference"] = {
         "ms": round(per_d["dense"], 4), "TFLOP/s": round(fld / per_d["dense"] / 1e9, 1),
@@ -429,6 +442,16 @@ def extra_all(steps):
     for key in ("dx_fp8", "dw_fp8"):
         out[f"backward_m32768_{key}"] = {"ms": round(per[key], 4), "TFLOP/s": round(fl / per[key] / 1e9, 1),
                                         "mfma_frac_fp8": round(fl / per[key] / 1e9 / MFMA_FP8_PEAK_TFLOPS, 4)}
+    shares8 = {}
+    for pct, hot_rows in (("60", 19660),) + HOT_SHARES:
+        gsx = torch.tensor(workloads.hot_expert_sizes(hot_rows=hot_rows), dtype=torch.int32, device="cuda")
+        _, _, per_x = timed_ops([
+            ("split", lambda: rd.trans_ragged_dot_fp8(x8, dy8, gsx, out=dw8)),
+            ("unsplit", lambda: rd.trans_ragged_dot_fp8(x8, dy8, gsx, out=dw8, row_split=False)),
+        ], steps, 3)
+        shares8[pct] = {key: round(ms, 4) for key, ms in per_x.items()}
+    hot_shares["fp8"] = shares8
+    out["backward_m32768_hot_expert_dw_by_share"] = hot_shares
     del dy8, w8, x8, dx, dw8
     torch.cuda.empty_cache()
     d = workloads.make(4, "cuda", parts=("x", "w", "fused", "d_out"))
