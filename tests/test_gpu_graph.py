@@ -100,3 +100,41 @@ def test_moe_mlp_training_step_graph_replays_follow_device_group_sizes():
         torch.cuda.synchronize()
         for name, a, b in zip(("out", "dx", "dwi", "dwo"), got, want):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"replay {i}: {name} differs from eager"
+
+
+def test_window_limit_forward_graph_replays_follow_device_scalars():
+    """A window+limit forward (the 128 x 256 eight-wave tile, whose window calls zero the rows outside the
+    window between their contraction steps) captured once and replayed after device-side rewrites of
+    group_sizes, the window offset and the limit; every replay bitwise equal to eager into a fresh
+    buffer filled the same way."""
+    say("graph capture of a window+limit forward")
+    G, gl, m, k, n = 16, 4, 6144, 256, 512
+    x = bf16_normal((m, k), 1.0, 90, DEV)
+    w = bf16_normal((gl, k, n), 0.05, 91, DEV)
+    gs = torch.from_numpy(workloads.random_sizes(G, m - 200, seed=92, empty=(3,))).to(DEV)
+    off = torch.tensor([2], dtype=torch.int32, device=DEV)
+    lim = torch.tensor([m - 500], dtype=torch.int32, device=DEV)
+    out = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    with rd.tuning(fwd_tile=14):
+        rd.ragged_dot(x, w, gs, off, lim, out=out)  # eager warm-up
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            rd.ragged_dot(x, w, gs, off, lim, out=out)
+    cases = [(workloads.random_sizes(G, m - 200, seed=93), 0, m), (workloads.random_sizes(G, m, seed=94), 5, 3000),
+             (workloads.random_sizes(G, m - 1000, seed=95, empty=(6, 7)), 12, 100), (workloads.random_sizes(G, m - 200, seed=92, empty=(3,)), 2, m - 500)]
+    for i, (sizes, o, l) in enumerate(cases):
+        gs.copy_(torch.from_numpy(sizes).to(DEV))  # device-side rewrites, outside the graph
+        off.fill_(o)
+        lim.fill_(l)
+        out.view(torch.int16).fill_(0x7F7F)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        want = torch.empty_like(out)
+        want.view(torch.int16).fill_(0x7F7F)
+        with rd.tuning(fwd_tile=14):
+            rd.ragged_dot(x, w, gs, off, lim, out=want)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"replay {i} differs from eager"
