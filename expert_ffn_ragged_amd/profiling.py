@@ -289,7 +289,8 @@ def load_traffic(path):
     """{op: traffic bytes per launch} from a traffic summary whose digest matches the sources, else {}."""
     if not os.path.exists(path):
         return {}
-    text = open(path).read()
+    with open(path) as f:
+        text = f.read()
     m = re.search(r"^source digest: (\w+)", text, flags=re.M)
     if not m or m.group(1) != source_digest():
         return {}

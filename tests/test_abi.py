@@ -16,7 +16,8 @@ HEADER = os.path.join(ROOT, "include", "rd.h")
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    with open(HEADER) as f:
+        text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(rd_[a-z_0-9]+)\s*\(", text)))
 

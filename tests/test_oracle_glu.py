@@ -109,9 +109,9 @@ def test_glu_fwd_special_values(g, u, want, why):
 
 def exact_silu_times_up(g, u):
     """silu(g) * u in float64 (real-number reference)."""
-    g = g.astype(np.float64)
-    u = u.astype(np.float64)
-    with np.errstate(over="ignore", invalid="ignore"):
+    with np.errstate(over="ignore", invalid="ignore"):  # the sweeps include NaN and infinite gates
+        g = g.astype(np.float64)
+        u = u.astype(np.float64)
         return g * u / (1.0 + np.exp(-g))
 
 
@@ -133,7 +133,8 @@ def test_glu_fwd_every_gate_against_exact_math():
     exact = exact_silu_times_up(g, u)
     # where the float32 op sequence stays in range (exp(-g) finite, result normal or zero)
     ok = np.isfinite(g) & (g > -87.0) & np.isfinite(exact) & ((np.abs(exact) > 1e-37) | (exact == 0))
-    want = f32_to_bf16_bits(exact[ok].astype(np.float32))
+    with np.errstate(over="ignore"):  # exact values past the float32 range round to infinity, as the oracle's do
+        want = f32_to_bf16_bits(exact[ok].astype(np.float32))
     d = ulp_distance(got[ok], want)
     assert d.max() <= 1
     assert np.mean(d == 0) > 0.999
