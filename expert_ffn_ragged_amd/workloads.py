@@ -2,7 +2,7 @@
 
 This module only draws random numbers: it holds none of the method's
 arithmetic, and both the GPU path's tests and the oracle's tests take their
-inputs from it.  Recipe (also stated in the design doc):
+inputs from it.  Recipe:
 
 * group sizes come from ``numpy.random.default_rng(seed)`` (seed = workload
   number unless given): multinomial draws over a uniform or Zipf(s) profile,

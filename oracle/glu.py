@@ -11,7 +11,7 @@ valid-rows-only MoE kernels", the commit on valid rows:
 * the backward writes ``[d_gate | d_up]`` in one pass, rounded once, and maps
   -0 to +0.
 
-Readings (listed in the design doc): the page prints no backward formula; this
+Readings where the page is silent: it prints no backward formula; this
 oracle uses the derivative of ``g * sigmoid(g) * u`` in float32,
 ``d_up = d * silu(g)`` and ``d_gate = d * u * s * (1 + g * (1 - s))`` with
 ``s = 1 / (1 + exp(-g))``, evaluated left to right; the -0 -> +0 map applies

@@ -21,7 +21,7 @@ Definitions, from the pages:
   trainer: MoE wo FSDP sharding and valid-rows-only MoE kernels", the commit
   on valid rows).
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 
 * group sizes are clamped: a negative size counts as 0, and every boundary is
   clamped to ``[0, L]`` where ``L`` is the limit clamped to ``[0, m]``

@@ -17,7 +17,7 @@ backward):
   tolerance of 1e-4);
 * only rows ``[0, limit)`` of the packed buffer hold tokens.
 
-Readings (listed in the design doc): rows at or past ``L = clamp(limit, 0,
+Readings of the page: rows at or past ``L = clamp(limit, 0,
 rows)`` are neither read nor written (the page's kernel also writes zeros up
 to the end of the 1024-row block holding row ``limit - 1``; that is an
 artifact of its block size, not part of what it computes; since the page
