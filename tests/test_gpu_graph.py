@@ -138,3 +138,54 @@ def test_window_limit_forward_graph_replays_follow_device_scalars():
             rd.ragged_dot(x, w, gs, off, lim, out=want)
         torch.cuda.synchronize()
         assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"replay {i} differs from eager"
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_trans_row_split_graph_replays_follow_device_group_sizes(fp8):
+    """trans_ragged_dot with its row-split workspace, captured once.  The split plan is made on the device
+    from group_sizes, so replays after device-side rewrites (a hot expert, another hot expert, uniform sizes,
+    two long groups) split different groups: the workspace header (split count, first split group) matches an
+    eager call's, the hot expert named is the one of the current sizes, and every replay is bitwise equal to
+    the eager call with a workspace of its own."""
+    say(f"graph capture of trans_ragged_dot with the row split (fp8={fp8})")
+    m, k, n, G = 8192, 256, 512, 8
+    cases = [np.array(c, dtype=np.int32) for c in ([6000, 310, 0, 502, 377, 250, 400, 353],
+                                                   [300, 200, 500, 0, 5500, 700, 492, 500],
+                                                   [1024] * 8,
+                                                   [3000, 3100, 0, 500, 600, 400, 292, 300])]
+    if fp8:
+        gen = [torch.Generator(device=DEV).manual_seed(s) for s in (95, 96)]
+        x = torch.randn((m, k), generator=gen[0], device=DEV).to(torch.float8_e4m3fn)
+        dy = torch.randn((m, n), generator=gen[1], device=DEV).to(torch.float8_e4m3fn)
+        call = rd.trans_ragged_dot_fp8
+    else:
+        x = bf16_normal((m, k), 1.0, 95, DEV)
+        dy = bf16_normal((m, n), 1.0, 96, DEV)
+        call = rd.trans_ragged_dot
+    gs = torch.from_numpy(cases[0]).to(DEV)
+    ws = torch.zeros(rd.trans_workspace_size(m, k, n, G), dtype=torch.uint8, device=DEV)
+    out = torch.empty((G, k, n), dtype=torch.float32, device=DEV)
+    call(x, dy, gs, out=out, workspace=ws)  # eager warm-up
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(x, dy, gs, out=out, workspace=ws)
+    ws_eager = torch.zeros_like(ws)
+    for i, sizes in enumerate(cases):
+        gs.copy_(torch.from_numpy(sizes).to(DEV))  # device-side rewrite, outside the graph
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got, head_replay = out.clone(), ws[:16].view(torch.int32).cpu().tolist()
+        want = torch.full_like(out, float("nan"))
+        call(x, dy, gs, out=want, workspace=ws_eager)
+        torch.cuda.synchronize()
+        head_eager = ws_eager[:16].view(torch.int32).cpu().tolist()
+        # header: [split groups, BM, BN, then (group, chunks, first chunk) per split group]
+        assert head_replay[0] == head_eager[0], f"replay {i}: {head_replay[0]} groups split, eager {head_eager[0]}"
+        if head_replay[0] > 0:
+            assert head_replay[3] == head_eager[3], f"replay {i}: split group {head_replay[3]}, eager {head_eager[3]}"
+        if i in (0, 1):
+            assert head_replay[0] > 0 and head_replay[3] == int(np.argmax(sizes)), f"replay {i}: header {head_replay}"
+        assert torch.equal(got.view(torch.int32), want.view(torch.int32)), f"replay {i} differs from eager"
