@@ -120,6 +120,8 @@ int rd_forward_trans_rhs(const void* x, const void* w, const int32_t* group_size
 int rd_forward_glu(const void* x, const void* wi, const int32_t* group_sizes, int32_t num_groups,
                    const int32_t* group_offset, int32_t num_local, const int32_t* limit, void* act,
                    void* fused, int64_t m, int64_t k, int64_t h, void* stream) {
+  if (h <= 0) return RD_EINVAL;
+  if (h >= (int64_t(1) << 30)) return RD_EUNSUPPORTED;  // the weight's width 2h stays below 2^31
   int st = check_dims(m, k, 2 * h);
   if (st != RD_OK) return st;
   st = check_groups(num_groups, group_offset, num_local);

@@ -7,7 +7,9 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
+import torch
 
 from expert_ffn_ragged_amd import rd
 
@@ -263,3 +265,58 @@ def test_noalloc_rejects_sizes_beyond_its_scratch_before_launching(lib):
     assert b"scratch" in lib.rd_status_string(st)
     # the decode step of 64 tokens x top-8 over 128 experts fits
     assert 0 < lib.rd_forward_workspace_size(512, 4096, 1536, 128, 0) <= rd.RD_NOALLOC_SCRATCH_BYTES
+
+
+# Extreme sizes and counts for the fuzz below (every data pointer NULL, so no call can pass validation
+# into a launch: each must return a status, and RD_OK only when there are no rows to process).
+_SIZES = [-(1 << 63), -(1 << 31), -1, 0, 1, 7, 8, 16, 24, 64, 136, 4096, (1 << 31) - 1, 1 << 31, 1 << 32,
+          (1 << 40) + 8, 1 << 62, (1 << 63) - 1]
+_COUNTS = [-(1 << 31), -1, 0, 1, 3, 8, 1024, 1025, (1 << 31) - 1]
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="host-side fuzz; kept off machines with a GPU")
+def test_null_pointer_fuzz_returns_a_status_for_any_sizes(lib):
+    """Every entry point with NULL data pointers and sizes drawn from extremes (negative, zero, odd, at and
+    past 2^31 / 2^32 / 2^63): a status from the header's list, RD_OK only with nothing to process, and the
+    workspace sizes never crash.  (Found a signed overflow of 2 * h in the fused GLU forward's checks.)"""
+    rng = np.random.default_rng(7)
+    pick = lambda xs: int(xs[rng.integers(len(xs))])
+    ok_status = {rd.RD_OK, rd.RD_EINVAL, rd.RD_EUNSUPPORTED}
+    # (name, argument kinds, index of the row count): s = int64 size, g = int32 count, d = dtype, w = bytes
+    calls = [("rd_forward", "nnngngnndsssnwn", 9), ("rd_forward_trans_rhs", "nnngngnndsssnwn", 9),
+             ("rd_forward_noalloc", "nnngngnndsssn", 9), ("rd_forward_fp8", "nnngngnndsssn", 9),
+             ("rd_forward_trans_rhs_fp8", "nnngngnndsssn", 9), ("rd_trans", "nnngngnndsssnwn", 9),
+             ("rd_trans_fp8", "nnngngnndsssnwn", 9), ("rd_forward_glu", "nnngngnnnsssn", 9),
+             ("rd_glu_fwd", "nnnssn", 3), ("rd_glu_bwd", "nnnnssn", 4), ("rd_unsort_bwd_rows", "nnnnnnssn", 6),
+             ("rd_zero_rows_from_limit", "nnssn", None)]  # a NULL limit leaves nothing to zero: RD_OK
+    for name, kinds, rows_at in calls:
+        f = getattr(lib, name)
+        for _ in range(600):
+            args = []
+            for c in kinds:
+                if c == "s":
+                    args.append(pick(_SIZES))
+                elif c == "g":
+                    args.append(pick(_COUNTS))
+                elif c == "d":
+                    args.append(pick([-1, 0, 1, 2, 7]))
+                elif c == "w":
+                    args.append(pick([0, 1, 256, 1 << 40]))
+                else:
+                    args.append(None)
+            st = f(*args)
+            assert st in ok_status, (name, args, st)
+            if st == rd.RD_OK and rows_at is not None:
+                assert args[rows_at] == 0, (name, args)
+    for _ in range(2000):
+        m, k, n = pick(_SIZES), pick(_SIZES), pick(_SIZES)
+        lib.rd_forward_workspace_size(m, k, n, pick(_COUNTS), pick([0, 1]))
+        lib.rd_trans_workspace_size(m, k, n, pick(_COUNTS))
+
+
+def test_fused_glu_forward_rejects_widths_past_the_limit(lib):
+    """h is checked before the weight width 2h is formed."""
+    for h, want in ((-5, rd.RD_EINVAL), (0, rd.RD_EINVAL), (1 << 30, rd.RD_EUNSUPPORTED),
+                    ((1 << 63) - 1, rd.RD_EUNSUPPORTED)):
+        st = lib.rd_forward_glu(None, None, None, 8, None, 8, None, None, None, 64, 128, h, None)
+        assert st == want, (h, st)
