@@ -112,10 +112,24 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream):
+def _launch(fn, tensors, stream, *args):
+    """Call C entry point ``fn(*args, stream)`` with the one GPU that every tensor of the call lives on
+    made current (the library sizes its grids, and finds its per-GPU scratch, on the current device);
+    ``stream`` None means that GPU's current torch stream."""
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"operands on {dev} and {t.device}: every tensor of a call must be on one GPU")
     if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+        stream = torch.cuda.current_stream(dev)
+    elif stream.device != dev:
+        raise ValueError(f"stream on {stream.device}, operands on {dev}")
+    with torch.cuda.device(dev):
+        _check(fn(*args, ctypes.c_void_p(stream.cuda_stream)))
 
 
 def _on_stream(stream, *tensors):
@@ -213,9 +227,9 @@ def ragged_dot(x, w, group_sizes, group_offset=None, limit=None, trans_rhs=False
     if fresh:
         _on_stream(stream, out)
     fn = lib.rd_forward_trans_rhs if trans_rhs else lib.rd_forward
-    _check(fn(_ptr(x), _ptr(w), _ptr(group_sizes), group_sizes.numel(), _ptr(group_offset), gl,
-              _ptr(limit), _ptr(out), _DTYPES[out.dtype], m, k, n,
-              _ptr(workspace) if ws_bytes else None, ws_bytes, _stream(stream)))
+    _launch(fn, (x, w, group_sizes, group_offset, limit, out, workspace if ws_bytes else None), stream,
+            _ptr(x), _ptr(w), _ptr(group_sizes), group_sizes.numel(), _ptr(group_offset), gl, _ptr(limit), _ptr(out),
+            _DTYPES[out.dtype], m, k, n, _ptr(workspace) if ws_bytes else None, ws_bytes)
     return out
 
 
@@ -238,8 +252,9 @@ def ragged_dot_noalloc(x, w, group_sizes, group_offset=None, limit=None, out=Non
     _need(out, "out", out.dtype, 2)
     if tuple(out.shape) != (m, n) or out.dtype not in _DTYPES:
         raise ValueError("out must be [m, n] bf16 or float32")
-    _check(library().rd_forward_noalloc(_ptr(x), _ptr(w), _ptr(group_sizes), group_sizes.numel(), _ptr(group_offset),
-                                        gl, _ptr(limit), _ptr(out), _DTYPES[out.dtype], m, k, n, _stream(stream)))
+    _launch(library().rd_forward_noalloc, (x, w, group_sizes, group_offset, limit, out), stream,
+            _ptr(x), _ptr(w), _ptr(group_sizes), group_sizes.numel(), _ptr(group_offset), gl, _ptr(limit), _ptr(out),
+            _DTYPES[out.dtype], m, k, n)
     return out
 
 
@@ -269,8 +284,9 @@ def ragged_dot_fp8(x, w, group_sizes, group_offset=None, limit=None, trans_rhs=F
     if tuple(out.shape) != (m, n) or out.dtype not in _DTYPES:
         raise ValueError("out must be [m, n] bf16 or float32")
     fn = library().rd_forward_trans_rhs_fp8 if trans_rhs else library().rd_forward_fp8
-    _check(fn(_ptr(x), _ptr(w), _ptr(group_sizes), group_sizes.numel(), _ptr(group_offset), gl, _ptr(limit),
-              _ptr(out), _DTYPES[out.dtype], m, k, n, _stream(stream)))
+    _launch(fn, (x, w, group_sizes, group_offset, limit, out), stream,
+            _ptr(x), _ptr(w), _ptr(group_sizes), group_sizes.numel(), _ptr(group_offset), gl, _ptr(limit), _ptr(out),
+            _DTYPES[out.dtype], m, k, n)
     return out
 
 
@@ -307,9 +323,9 @@ def trans_ragged_dot_fp8(x, dy, group_sizes, num_local=None, group_offset=None, 
         if ws_bytes:
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
             _on_stream(stream, workspace)
-    _check(lib.rd_trans_fp8(_ptr(x), _ptr(dy), _ptr(group_sizes), group_sizes.numel(), _ptr(group_offset), gl,
-                            _ptr(limit), _ptr(out), _DTYPES[out.dtype], m, k, n,
-                            _ptr(workspace) if ws_bytes else None, ws_bytes, _stream(stream)))
+    _launch(lib.rd_trans_fp8, (x, dy, group_sizes, group_offset, limit, out, workspace if ws_bytes else None), stream,
+            _ptr(x), _ptr(dy), _ptr(group_sizes), group_sizes.numel(), _ptr(group_offset), gl, _ptr(limit),
+            _ptr(out), _DTYPES[out.dtype], m, k, n, _ptr(workspace) if ws_bytes else None, ws_bytes)
     return out
 
 
@@ -349,8 +365,9 @@ def ragged_dot_glu(x, wi, group_sizes, group_offset=None, limit=None, act=None, 
         _need(fused, "fused", torch.bfloat16, 2)
         if tuple(fused.shape) != (m, h2):
             raise ValueError("fused must be [m, 2h]")
-    _check(library().rd_forward_glu(_ptr(x), _ptr(wi), _ptr(group_sizes), group_sizes.numel(), _ptr(group_offset),
-                                    gl, _ptr(limit), _ptr(act), _ptr(fused), m, k, h, _stream(stream)))
+    _launch(library().rd_forward_glu, (x, wi, group_sizes, group_offset, limit, act, fused), stream,
+            _ptr(x), _ptr(wi), _ptr(group_sizes), group_sizes.numel(), _ptr(group_offset), gl, _ptr(limit),
+            _ptr(act), _ptr(fused), m, k, h)
     return act if fused is None else (act, fused)
 
 
@@ -390,9 +407,9 @@ def trans_ragged_dot(x, dy, group_sizes, num_local=None, group_offset=None, limi
             _on_stream(stream, workspace)
     if fresh:
         _on_stream(stream, out)
-    _check(lib.rd_trans(_ptr(x), _ptr(dy), _ptr(group_sizes), group_sizes.numel(), _ptr(group_offset), gl,
-                        _ptr(limit), _ptr(out), _DTYPES[out.dtype], m, k, n,
-                        _ptr(workspace) if ws_bytes else None, ws_bytes, _stream(stream)))
+    _launch(lib.rd_trans, (x, dy, group_sizes, group_offset, limit, out, workspace if ws_bytes else None), stream,
+            _ptr(x), _ptr(dy), _ptr(group_sizes), group_sizes.numel(), _ptr(group_offset), gl, _ptr(limit),
+            _ptr(out), _DTYPES[out.dtype], m, k, n, _ptr(workspace) if ws_bytes else None, ws_bytes)
     return out
 
 
@@ -415,7 +432,8 @@ def glu_fwd(fused, limit=None, out=None, stream=None):
     _need(out, "out", torch.bfloat16, 2)
     if tuple(out.shape) != (rows, h):
         raise ValueError("out must be [rows, h]")
-    _check(library().rd_glu_fwd(_ptr(fused), _ptr(limit), _ptr(out), rows, h, _stream(stream)))
+    _launch(library().rd_glu_fwd, (fused, limit, out), stream,
+            _ptr(fused), _ptr(limit), _ptr(out), rows, h)
     return out
 
 
@@ -434,7 +452,8 @@ def glu_bwd(fused, d_out, limit=None, out=None, stream=None):
     _need(out, "out", torch.bfloat16, 2)
     if tuple(out.shape) != (rows, two_h):
         raise ValueError("out must be [rows, 2h]")
-    _check(library().rd_glu_bwd(_ptr(fused), _ptr(d_out), _ptr(limit), _ptr(out), rows, h, _stream(stream)))
+    _launch(library().rd_glu_bwd, (fused, d_out, limit, out), stream,
+            _ptr(fused), _ptr(d_out), _ptr(limit), _ptr(out), rows, h)
     return out
 
 
@@ -461,8 +480,8 @@ def unsort_bwd_rows(g, y, w, limit=None, grad=None, dot=None, stream=None):
     _need(dot, "dot", torch.float32, 1)
     if tuple(grad.shape) != (rows, hidden) or dot.shape[0] != rows:
         raise ValueError("grad must be [rows, hidden] and dot [rows]")
-    _check(library().rd_unsort_bwd_rows(_ptr(g), _ptr(y), _ptr(w), _ptr(limit), _ptr(grad), _ptr(dot), rows, hidden,
-                                        _stream(stream)))
+    _launch(library().rd_unsort_bwd_rows, (g, y, w, limit, grad, dot), stream,
+            _ptr(g), _ptr(y), _ptr(w), _ptr(limit), _ptr(grad), _ptr(dot), rows, hidden)
     return grad, dot
 
 
@@ -476,6 +495,6 @@ def zero_rows_from_limit(buf, limit, stream=None):
         raise ValueError("buf must be a contiguous GPU tensor")
     rows = buf.shape[0]
     row_bytes = buf[0].numel() * buf.element_size() if rows else 16
-    _check(library().rd_zero_rows_from_limit(_ptr(buf) if rows else None, _ptr(limit), rows, row_bytes,
-                                             _stream(stream)))
+    _launch(library().rd_zero_rows_from_limit, (buf, limit), stream,
+            _ptr(buf) if rows else None, _ptr(limit), rows, row_bytes)
     return buf

@@ -320,3 +320,17 @@ def test_fused_glu_forward_rejects_widths_past_the_limit(lib):
                     ((1 << 63) - 1, rd.RD_EUNSUPPORTED)):
         st = lib.rd_forward_glu(None, None, None, 8, None, 8, None, None, None, 64, 128, h, None)
         assert st == want, (h, st)
+
+
+def test_binding_rejects_operands_on_two_gpus_before_any_call():
+    """The binding makes the operands' GPU current for each call; operands (or a stream) on another GPU
+    are refused before anything reaches the library."""
+    from types import SimpleNamespace
+    calls = []
+    on0 = SimpleNamespace(device=torch.device("cuda", 0))
+    on1 = SimpleNamespace(device=torch.device("cuda", 1))
+    with pytest.raises(ValueError, match="one GPU"):
+        rd._launch(lambda *a: calls.append(a), (on0, None, on1), None)
+    with pytest.raises(ValueError, match="stream on"):
+        rd._launch(lambda *a: calls.append(a), (on0, on0), SimpleNamespace(device=torch.device("cuda", 1)))
+    assert calls == []
