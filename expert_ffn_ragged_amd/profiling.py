@@ -270,6 +270,7 @@ def loadpath_summary(dirs, command, title=DEFAULT_TITLE):
              "in cycles per L1 -> L2 read request.", "",
              "| op | kernel | " + " | ".join(PER_CU) + " | read latency (cycles) | L2 hit rate |",
              "|---|---|" + "---|" * (len(PER_CU) + 2)]
+    readings = []
     for name, ctrs in sorted(means.items(), key=lambda kv: str(op_of(kv[0]))):
         if op_of(name) is None or "GRBM_GUI_ACTIVE" not in ctrs:
             continue
@@ -282,6 +283,17 @@ def loadpath_summary(dirs, command, title=DEFAULT_TITLE):
         lat = f"{ctrs['TCP_TCC_READ_REQ_LATENCY'][0] / req:.0f}" if req and "TCP_TCC_READ_REQ_LATENCY" in ctrs else "-"
         hit = f"{ctrs['TCC_HIT'][0] / req:.2f}" if req and "TCC_HIT" in ctrs else "-"
         lines.append(f"| {op_of(name)} | `{name}` | " + " | ".join(frac(c) for c in PER_CU) + f" | {lat} | {hit} |")
+        if "grouped_gemm" in name and all(c in ctrs for c in ("TCP_PENDING_STALL_CYCLES", "TD_TD_BUSY", "TD_TC_STALL")):
+            readings.append(
+                f"- {op_of(name)}: the vector L1 of each CU waits on data pending from L2 "
+                f"{100 * float(frac('TCP_PENDING_STALL_CYCLES')):.0f} % of its cycles. The data-return unit is "
+                f"{100 * float(frac('TD_TD_BUSY')):.0f} % busy, "
+                f"{100 * float(frac('TD_TC_STALL')):.0f} % of the cycles stalled on the cache. The L2 hit rate is "
+                f"{hit}, and {lat} cycles is the mean read latency.")
+    if readings:
+        lines += ["", "What caps the grouped GEMMs: the load stream into each CU, not the MFMAs. A stage is "
+                  "complete only when its slowest line has arrived, so the lines that miss L2 hold up each stage.",
+                  ""] + readings
     return "\n".join(lines) + "\n"
 
 
