@@ -472,8 +472,11 @@ def extra_all(steps):
     fl = 2.0 * win_rows * d["k"] * d["n"]
     nb = win_rows * d["k"] * 2 + d["w"].numel() * 2 + L * d["n"] * 2
     ms = per["window_ragged_dot"]
+    tr = measured_traffic(PACKED_TRAFFIC_FILE)
     out["window_limit_ragged_dot"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1),
-                                      "GB/s": round(nb / ms / 1e6, 1)}
+                                      "GB/s": round(nb / ms / 1e6, 1), "hbm_frac": round(nb / ms / 1e6 / HBM_PEAK_GBS, 4),
+                                      "algorithmic_bytes": int(nb),
+                                      "traffic": None if "ragged_dot" not in tr else int(tr["ragged_dot"])}
     # the same forward with the heaviest ranks of Zipf(1.1) sizes inside the window (a hot window)
     hs = workloads.hot_window_sizes()
     gsh = torch.tensor(hs, dtype=torch.int32, device="cuda")
@@ -484,7 +487,6 @@ def extra_all(steps):
         "ms": round(per_h["hot"], 4), "TFLOP/s": round(flh / per_h["hot"] / 1e9, 1),
         "mfma_frac": round(flh / per_h["hot"] / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4), "window_rows": hrows,
         "sizes": "Zipf(1.1) over 256 groups, the 32 heaviest ranks in the window 96..127"}
-    tr = measured_traffic(PACKED_TRAFFIC_FILE)
     for key, nbytes in (("glu_fwd", L * h * 6), ("glu_bwd", L * h * 10)):
         out[f"window_limit_{key}"] = {"ms": round(per[key], 4), "GB/s": round(nbytes / per[key] / 1e6, 1),
                                       "hbm_frac": round(nbytes / per[key] / 1e6 / HBM_PEAK_GBS, 4),
@@ -814,14 +816,17 @@ def profile_run(which, steps, warmup, cold=False, settle_steps=0):
         ws = torch.empty(max(rd.library().rd_forward_workspace_size(d["m"], d["k"], d["n"], d["G"], 0), 16),
                          dtype=torch.uint8, device="cuda")
         ops = [lambda: rd.ragged_dot(d["x"], d["w"], d["gs"], out=o, workspace=ws)]
-    else:  # the packed expert buffer: GLU forward / backward and the unsort backward at limit 126156
-        d = workloads.make(4, "cuda", parts=("fused", "d_out", "ug", "uy", "uw"))
+    else:  # the packed expert buffer at limit 126156: the window+limit forward, GLU fwd / bwd, unsort backward
+        d = workloads.make(4, "cuda", parts=("x", "w", "fused", "d_out", "ug", "uy", "uw"))
         lim = torch.tensor([d["limit"]], dtype=torch.int32, device="cuda")
+        off = torch.tensor([d["offset"]], dtype=torch.int32, device="cuda")
+        o = torch.empty((d["m"], d["n"]), dtype=torch.bfloat16, device="cuda")
         g = torch.empty((d["m"], d["n"]), dtype=torch.bfloat16, device="cuda")
         gb = torch.empty((d["m"], 2 * d["n"]), dtype=torch.bfloat16, device="cuda")
         grad = torch.empty((d["m"], d["k"]), dtype=torch.bfloat16, device="cuda")
         dot = torch.empty((d["m"],), dtype=torch.float32, device="cuda")
-        ops = [lambda: rd.glu_fwd(d["fused"], lim, out=g), lambda: rd.glu_bwd(d["fused"], d["d_out"], lim, out=gb),
+        ops = [lambda: rd.ragged_dot(d["x"], d["w"], d["gs"], off, lim, out=o),
+               lambda: rd.glu_fwd(d["fused"], lim, out=g), lambda: rd.glu_bwd(d["fused"], d["d_out"], lim, out=gb),
                lambda: rd.unsort_bwd_rows(d["ug"], d["uy"], d["uw"], lim, grad=grad, dot=dot)]
     if settle_steps:
         settle([(None, fn) for fn in ops], settle_steps, cold)
